@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Throughput of the branch-attention hot path on one MI355X.
+
+One step = one forward and one backward pass of the whole path over one batch:
+main-sequence attention of every row over its causal main prefix, the
+branch-local attention, the log-sum-exp merge, the backward preprocess, and the
+main-sequence and branch-local backward passes. Default workload: one rank's
+share of a 256K-token sequence in a 16-chunk zigzag layout (rank 3 of CP=8:
+chunks 3 and 12 hold the queries, keys 0..212991), GQA 32q/8kv, head_dim 128,
+EAGLE-3 TTT depth-7 branches on every local position, bf16, synthetic seeded
+inputs already resident in HBM.
+
+Prints one JSON line. value = algorithmic fwd+bwd TFLOP/s: 4*d*Hq and 10*d*Hq
+flops per visible (row, key) pair for the forward and the backward.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+METRIC = "branch-attention fwd+bwd TFLOP/s and % bf16 MFMA peak, 256K-ctx 1-GPU share"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "speculative_draft_branch_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {"main_fwd": ["main_fwd.hip", "common.hpp", "plan.hpp"],
+                  "main_bwd": ["main_bwd.hip", "common.hpp", "plan.hpp"]}
+
+
+def traffic_from_profile(kernel, workload):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        if d.get("source_hash") != kernel_source_hash(KERNEL_SOURCES[kernel]):
+            return None
+        return float(d["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def row_pairs(w, rows):
+    """Visible keys of each combined row (main prefix plus own branch keys)."""
+    import numpy as np
+    out = []
+    for r in rows:
+        if r < w.Nq:
+            t = int(w.q_pos[r])
+            s = int(np.searchsorted(w.cu_seqlens, t, side="right") - 1)
+            out.append(t - int(w.cu_seqlens[s]) + 1)
+        else:
+            b = r - w.Nq
+            m = int(np.searchsorted(w.cu_branch, b, side="right") - 1)
+            a = int(w.anchors[m])
+            s = int(np.searchsorted(w.cu_seqlens, a, side="right") - 1)
+            L = int(w.cu_branch[m + 1] - w.cu_branch[m])
+            j = b - int(w.cu_branch[m]) + 1
+            out.append(a - int(w.cu_seqlens[s]) + 1 + (L if w.modes[m] == 1 else j))
+    return out
+
+
+def cpu_baseline(w, t, seconds):
+    """The CPU oracle, as it is, on a bounded random sample of rows of the same
+    workload: forward of each sampled row plus its backward contributions."""
+    import numpy as np
+    import oracle
+    from workloads.inputs import to_f32
+
+    class View:
+        def __init__(self, a):
+            self.a, self.shape = a, a.shape
+
+        def __getitem__(self, i):
+            return to_f32(self.a[i])
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(x.get("num_threads", 0)) for x in threadpool_info()] + [0])
+    except Exception:
+        cores = 0
+    cores = cores or len(os.sched_getaffinity(0))
+    p = oracle.Problem.from_workload(w)
+    tv = {k: View(v) for k, v in t.items()}
+    hm = oracle.branch_attention._HeadMajor(p, tv, np.float64)   # one-time layout copy, not timed
+    acc = {"dk": np.zeros((w.N, w.num_kv_heads, w.head_dim)), "dv": np.zeros((w.N, w.num_kv_heads, w.head_dim)),
+           "dkb": np.zeros((w.Rb, w.num_kv_heads, w.head_dim)), "dvb": np.zeros((w.Rb, w.num_kv_heads, w.head_dim))}
+    rng = np.random.default_rng(1234)
+    R = w.Nq + w.Rb
+    done, flops, t0 = [], 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds or len(done) < 2:
+        r = int(rng.integers(0, R))
+        oracle.forward_rows(p, tv, [r], _hm=hm)
+        oracle.backward_rows(p, tv, [r], acc, _hm=hm)
+        done.append(r)
+    el = time.perf_counter() - t0
+    n_pairs = sum(row_pairs(w, done))
+    flops = n_pairs * w.num_q_heads * (4 + 10) * w.head_dim
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{len(done)} uniformly drawn rows (all {w.num_q_heads} heads) of {w.name}: fp64 numpy "
+                       f"forward + backward of each row over its visible keys ({n_pairs} row-key pairs), "
+                       f"{el:.1f} s; fwd+bwd flops counted as in value"),
+            "seconds": el}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="ctx256k_rank3")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only: the path runs one GPU's share; "
+                                   "run with --gpus 1", "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import speculative_draft_branch_amd as sda
+    import workloads as W
+    from workloads.inputs import make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = W.get(args.workload)
+    log(f"workload {w.name}: N={w.N} Nq={w.Nq} Rb={w.Rb} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim}")
+    t_gen = time.time()
+    t = make_inputs(w, grads=True)
+    log(f"inputs generated in {time.time() - t_gen:.1f} s")
+    g = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() for k, v in t.items()}
+    t_plan = time.time()
+    plan = sda.Plan.from_workload(w)
+    log(f"plan built in {time.time() - t_plan:.2f} s: {plan.n_qtiles} query tiles, {plan.n_ktiles} key tiles")
+    dev = g["q"].device
+    hq, d = w.num_q_heads, w.head_dim
+    o, ob = torch.empty_like(g["q"]), torch.empty_like(g["qb"])
+    lse = torch.empty((hq, w.Nq), dtype=torch.float32, device=dev)
+    lseb = torch.empty((hq, w.Rb), dtype=torch.float32, device=dev)
+    gr = [torch.empty_like(g[k]) for k in ("q", "k", "v", "qb", "kb", "vb")]
+    ws_f, ws_b = sda.workspace(plan, 0, dev), sda.workspace(plan, 1, dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sda.branch_attn_fwd(plan, g["q"], g["k"], g["v"], g["qb"], g["kb"], g["vb"], o, lse, ob, lseb, ws_f)
+        sda.branch_attn_bwd(plan, g["q"], g["k"], g["v"], g["qb"], g["kb"], g["vb"], o, lse, ob, lseb,
+                            g["do"], g["dob"], *gr, ws_b)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup step {i} done")
+    sda.timing_reset()
+    sda.timing_enable(True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sda.timing_enable(False)
+    ms = e0.elapsed_time(e1) / args.steps
+    kern = sda.timing_read()
+    log(f"timed {args.steps} steps: {ms:.1f} ms/step")
+
+    pairs = sum(plan.pairs)
+    flops_fwd, flops_bwd = plan.flops_fwd(), plan.flops_bwd()
+    value = (flops_fwd + flops_bwd) / (ms * 1e-3) / 1e12
+    fwd_ms = sum(kern[k][0] for k in ("metadata_upload", "main_fwd", "branch_local_fwd", "lse_merge")) / args.steps
+    bwd_ms = ms - fwd_ms
+    main_pairs = plan.pairs[0] + plan.pairs[1]
+    algo = {"main_fwd": 4 * d * hq * main_pairs, "main_bwd": 10 * d * hq * main_pairs}
+    dominant = max(algo, key=lambda k: kern[k][0])
+    dom_ms = kern[dominant][0] / max(1, kern[dominant][1])
+    achieved = algo[dominant] / (dom_ms * 1e-3) / 1e12
+    traffic = traffic_from_profile(dominant, w.name)
+    fwd_main_ms = kern["main_fwd"][0] / max(1, kern["main_fwd"][1])
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens_total": 16 * 16384 if w.name == "ctx256k_rank3" else w.N,
+                   "main_keys": w.N, "main_query_rows": w.Nq, "branch_rows": w.Rb,
+                   "q_heads": hq, "kv_heads": w.num_kv_heads, "head_dim": d,
+                   "description": w.description},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd_ms": round(fwd_ms, 3),
+        "bwd_ms": round(bwd_ms, 3),
+        "fwd_tflops": round(flops_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(flops_bwd / (bwd_ms * 1e-3) / 1e12, 2),
+        "main_fwd_frac_peak": round(4 * d * hq * main_pairs / (fwd_main_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kernels_ms_per_launch": {k: round(v[0] / max(1, v[1]), 3) for k, v in kern.items() if v[1]},
+        "roofline": {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on sampled rows for ~{args.cpu_seconds:.0f} s")
+        res["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -274,23 +274,31 @@ class _HeadMajor:
 
 
 def _row_fwd(p: Problem, hm: _HeadMajor, q_row: np.ndarray, r: int, dtype):
-    """One row, all heads: scores against its visible keys -> (O [Hq,d], LSE [Hq], P per head, keys)."""
+    """One row, all heads: scores against its visible keys.
+
+    Returns O [Hq,d], LSE [Hq], P [Hq, n_keys] and the key set (lo, hi, bk).
+    The q heads of one kv group are scored together against that group's keys.
+    """
     lo, hi, bk = row_keys(p, r)
+    n = hi - lo + 1 + len(bk)
     O = np.zeros((p.hq, p.d), dtype)
     L = np.zeros(p.hq, dtype)
-    Ps = []
-    for h in range(p.hq):
-        g = int(p.kv_head_of[h])
-        qh = np.asarray(q_row[h], dtype=dtype)
+    P = np.zeros((p.hq, n), dtype)
+    for g in range(p.hkv):
+        heads = np.nonzero(p.kv_head_of == g)[0]
+        if len(heads) == 0:
+            continue
+        qg = np.asarray(q_row[heads], dtype=dtype)                       # [G, d]
         kk = np.concatenate([hm.k[g][lo:hi + 1], _as(hm.kb[bk, g, :], dtype)])
         vv = np.concatenate([hm.v[g][lo:hi + 1], _as(hm.vb[bk, g, :], dtype)])
-        S = p.scale * (kk @ qh)
-        m = S.max()
-        L[h] = m + math.log(np.exp(S - m).sum())
-        P = np.exp(S - L[h])
-        O[h] = P @ vv
-        Ps.append(P)
-    return O, L, Ps, (lo, hi, bk)
+        S = p.scale * (qg @ kk.T)                                        # [G, n]
+        m = S.max(axis=1)
+        lse = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
+        Pg = np.exp(S - lse[:, None])
+        O[heads] = Pg @ vv
+        L[heads] = lse
+        P[heads] = Pg
+    return O, L, P, (lo, hi, bk)
 
 
 def forward_rows(p: Problem, t: Dict[str, np.ndarray], rows: Iterable[int], dtype=np.float64,
@@ -324,21 +332,23 @@ def backward_rows(p: Problem, t: Dict[str, np.ndarray], rows: Iterable[int], acc
         main = r < p.Nq
         q_row = t["q"][r] if main else t["qb"][r - p.Nq]
         do_row = t["do"][r] if main else t["dob"][r - p.Nq]
-        O, L, Ps, (lo, hi, bk) = _row_fwd(p, hm, q_row, r, dtype)
+        O, L, P, (lo, hi, bk) = _row_fwd(p, hm, q_row, r, dtype)
         nmain = hi - lo + 1
-        for h in range(p.hq):
-            g = int(p.kv_head_of[h])
-            doh = np.asarray(do_row[h], dtype=dtype)
-            qh = np.asarray(q_row[h], dtype=dtype)
+        for g in range(p.hkv):
+            heads = np.nonzero(p.kv_head_of == g)[0]
+            if len(heads) == 0:
+                continue
+            qg = np.asarray(q_row[heads], dtype=dtype)                   # [G, d]
+            dog = np.asarray(do_row[heads], dtype=dtype)                 # [G, d]
             kk = np.concatenate([hm.k[g][lo:hi + 1], _as(hm.kb[bk, g, :], dtype)])
             vv = np.concatenate([hm.v[g][lo:hi + 1], _as(hm.vb[bk, g, :], dtype)])
-            P = Ps[h]
-            D = float(doh @ O[h])
-            dS = P * (vv @ doh - D)
-            dQ[i, h] = p.scale * (dS @ kk)
+            Pg = P[heads]                                                # [G, n]
+            D = (dog * O[heads]).sum(axis=1)                             # [G]
+            dS = Pg * (dog @ vv.T - D[:, None])                          # [G, n]
+            dQ[i, heads] = p.scale * (dS @ kk)
             if acc is not None:
-                dk_c = p.scale * np.outer(dS, qh)
-                dv_c = np.outer(P, doh)
+                dk_c = p.scale * (dS.T @ qg)                             # [n, d]
+                dv_c = Pg.T @ dog                                        # [n, d]
                 acc["dk"][lo:hi + 1, g] += dk_c[:nmain]
                 acc["dv"][lo:hi + 1, g] += dv_c[:nmain]
                 acc["dkb"][bk, g] += dk_c[nmain:]

@@ -1,0 +1,34 @@
+// Host-side launchers of the device kernels (one per kernel family).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace ba {
+
+hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t st);
+hipError_t launch_lse_merge(int64_t rows, int heads, int d, const float *oa, const float *la, const float *ob,
+                            const float *lb, void *oo, ba_dtype_t out_dtype, float *lo, hipStream_t st);
+hipError_t launch_branch_local_fwd(const Meta &mt, ba_dtype_t dt, const void *qb, const void *kb, const void *vb,
+                                   float *o_loc, float *lse_loc, hipStream_t st);
+hipError_t launch_branch_local_bwd(const Meta &mt, ba_dtype_t dt, const void *qb, const void *kb, const void *vb,
+                                   const void *dob, const float *lseb, const float *delta, float *dq_acc,
+                                   void *dkb, void *dvb, hipStream_t st);
+hipError_t launch_bwd_preprocess(const Meta &mt, ba_dtype_t dt, const void *o, const void *d_o, const void *ob,
+                                 const void *d_ob, float *delta, hipStream_t st);
+hipError_t launch_convert_rows(const float *acc, int64_t n, void *out, ba_dtype_t dt, hipStream_t st);
+// float32 main-sequence kernels (plain wave-per-row form)
+hipError_t launch_main_fwd_f32(const Meta &mt, const float *q, const float *qb, const float *k, const float *v,
+                               float *o, float *lse, float *o_pre, float *lse_pre, hipStream_t st);
+hipError_t launch_main_bwd_f32(const Meta &mt, const float *q, const float *qb, const float *k, const float *v,
+                               const float *d_o, const float *d_ob, const float *lse, const float *lseb,
+                               const float *delta, float *dq_acc, float *dk, float *dv, hipStream_t st);
+// bf16 MFMA main-sequence kernels
+hipError_t launch_main_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *v,
+                                bf16 *o, float *lse, float *o_pre, float *lse_pre, hipStream_t st);
+hipError_t launch_main_bwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *v,
+                                const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
+                                const float *delta, float *dq_acc, bf16 *dk, bf16 *dv, hipStream_t st);
+
+}  // namespace ba

@@ -1,0 +1,346 @@
+// Plan construction: validation, per-row key ranges, query tiles, backward key
+// tiles and longest-first launch orders. Pure host code.
+//
+// Which keys a row sees (rcap.io explainer, paragraph on branch attention under
+// context parallelism; cere-bro wiki, "Mechanism"): a main row at packed
+// position t sees main keys cu[s]..t of its sequence s; every query of a branch
+// anchored at a sees main keys cu[s]..a. Rows whose prefix end is the same see
+// the same main keys, so the plan groups rows by prefix end: the main row at a
+// position, the branch rows anchored there and the q heads of one kv group all
+// share one K/V stream.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <numeric>
+
+#include "plan.hpp"
+
+namespace ba {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+ba_status_t set_error(ba_status_t st, const std::string &msg) {
+  g_last_error = msg;
+  return st;
+}
+
+const char *last_error() { return g_last_error.c_str(); }
+
+}  // namespace ba
+
+using namespace ba;
+
+namespace {
+
+ba_status_t validate_and_copy(const ba_problem_t *p, ba_plan *pl) {
+  if (!p) return set_error(BA_EINVAL, "problem is NULL");
+  if (p->dtype != BA_F32 && p->dtype != BA_BF16) return set_error(BA_EINVAL, "dtype must be BA_F32 or BA_BF16");
+  if (p->num_q_heads < 1 || p->num_kv_heads < 1) return set_error(BA_EINVAL, "head counts must be >= 1");
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return set_error(BA_EINVAL, "num_q_heads must be a multiple of num_kv_heads");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return set_error(BA_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if (!(p->softmax_scale >= 0.0f) || std::isinf(p->softmax_scale))
+    return set_error(BA_EINVAL, "softmax_scale must be finite and >= 0");
+  pl->dtype = p->dtype;
+  pl->hq = p->num_q_heads;
+  pl->hkv = p->num_kv_heads;
+  pl->d = p->head_dim;
+  pl->G = pl->hq / pl->hkv;
+  if (pl->G > kTileRows) return set_error(BA_EUNSUPPORTED, "more than 128 q heads per kv head");
+  pl->scale = p->softmax_scale > 0.0f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+
+  pl->kv_head_of.resize(pl->hq);
+  for (int h = 0; h < pl->hq; ++h) pl->kv_head_of[h] = p->kv_head_of ? p->kv_head_of[h] : h / pl->G;
+  pl->group_heads.assign((size_t)pl->hkv * pl->G, -1);
+  std::vector<int> fill(pl->hkv, 0);
+  for (int h = 0; h < pl->hq; ++h) {
+    int g = pl->kv_head_of[h];
+    if (g < 0 || g >= pl->hkv) return set_error(BA_EINVAL, "kv_head_of entry out of range");
+    if (fill[g] >= pl->G) return set_error(BA_EINVAL, "kv_head_of must give every kv head Hq/Hkv q heads");
+    pl->group_heads[(size_t)g * pl->G + fill[g]++] = h;
+  }
+
+  if (p->num_seqs < 1 || !p->cu_seqlens) return set_error(BA_EINVAL, "need num_seqs >= 1 and cu_seqlens");
+  pl->S = p->num_seqs;
+  pl->cu.assign(p->cu_seqlens, p->cu_seqlens + pl->S + 1);
+  if (pl->cu[0] != 0) return set_error(BA_EINVAL, "cu_seqlens[0] must be 0");
+  for (int s = 0; s < pl->S; ++s)
+    if (pl->cu[s + 1] < pl->cu[s]) return set_error(BA_EINVAL, "cu_seqlens must be non-decreasing");
+  pl->N = pl->cu[pl->S];
+
+  if (p->q_pos) {
+    if (p->num_q < 0) return set_error(BA_EINVAL, "num_q must be >= 0");
+    pl->q_pos.assign(p->q_pos, p->q_pos + p->num_q);
+    for (int64_t i = 0; i < p->num_q; ++i) {
+      if (pl->q_pos[i] < 0 || pl->q_pos[i] >= pl->N) return set_error(BA_EINVAL, "q_pos out of [0, N)");
+      if (i && pl->q_pos[i] <= pl->q_pos[i - 1]) return set_error(BA_EINVAL, "q_pos must be strictly increasing");
+    }
+  } else {
+    pl->q_pos.resize(pl->N);
+    std::iota(pl->q_pos.begin(), pl->q_pos.end(), 0);
+  }
+  pl->Nq = (int64_t)pl->q_pos.size();
+
+  if (p->num_anchors < 0) return set_error(BA_EINVAL, "num_anchors must be >= 0");
+  pl->A = p->num_anchors;
+  if (pl->A > 0 && !p->anchors) return set_error(BA_EINVAL, "anchors is NULL");
+  pl->anchors.assign(p->anchors, p->anchors + pl->A);
+  for (int64_t m = 0; m < pl->A; ++m) {
+    if (pl->anchors[m] < 0 || pl->anchors[m] >= pl->N) return set_error(BA_EINVAL, "anchor out of [0, N)");
+    if (m && pl->anchors[m] <= pl->anchors[m - 1]) return set_error(BA_EINVAL, "anchors must be strictly increasing");
+  }
+  pl->cu_branch.resize(pl->A + 1);
+  if (p->cu_branch) {
+    pl->cu_branch.assign(p->cu_branch, p->cu_branch + pl->A + 1);
+    if (pl->cu_branch[0] != 0) return set_error(BA_EINVAL, "cu_branch[0] must be 0");
+  } else {
+    if (p->branch_len < 0) return set_error(BA_EINVAL, "branch_len must be >= 0");
+    for (int64_t m = 0; m <= pl->A; ++m) {
+      int64_t v = m * (int64_t)p->branch_len;
+      if (v > INT32_MAX) return set_error(BA_EINVAL, "too many branch rows");
+      pl->cu_branch[m] = (int32_t)v;
+    }
+  }
+  for (int64_t m = 0; m < pl->A; ++m) {
+    int32_t L = pl->cu_branch[m + 1] - pl->cu_branch[m];
+    if (L < 0) return set_error(BA_EINVAL, "cu_branch must be non-decreasing");
+    if (L > kMaxBranch) return set_error(BA_EINVAL, "a branch has more than 32 rows");
+  }
+  pl->Rb = pl->cu_branch[pl->A];
+  pl->mode.resize(pl->A);
+  for (int64_t m = 0; m < pl->A; ++m) {
+    int md = p->mode ? (int)p->mode[m] : (int)p->uniform_mode;
+    if (md != BA_TTT && md != BA_BLOCK) return set_error(BA_EINVAL, "mode must be BA_TTT or BA_BLOCK");
+    pl->mode[m] = (uint8_t)md;
+  }
+  if (pl->Nq + pl->Rb > INT32_MAX / 2) return set_error(BA_EINVAL, "too many rows");
+  return BA_OK;
+}
+
+template <class T>
+size_t put(std::vector<uint8_t> &blob, size_t &cur, const std::vector<T> &v) {
+  size_t off = cur;
+  size_t bytes = v.size() * sizeof(T);
+  cur = align_up(cur + bytes, 256);
+  if (blob.size() < cur) blob.resize(cur, 0);
+  if (bytes) std::memcpy(blob.data() + off, v.data(), bytes);
+  return off;
+}
+
+void build(ba_plan *pl) {
+  const int64_t Nq = pl->Nq, Rb = pl->Rb, R = Nq + Rb;
+  // Per combined row: visible main key range [lo, hi].
+  std::vector<int32_t> row_lo(R), row_hi(R);
+  auto seq_of = [&](int32_t pos) {
+    return (int32_t)(std::upper_bound(pl->cu.begin(), pl->cu.end(), pos) - pl->cu.begin() - 1);
+  };
+  for (int64_t i = 0; i < Nq; ++i) {
+    int32_t t = pl->q_pos[i];
+    row_lo[i] = pl->cu[seq_of(t)];
+    row_hi[i] = t;
+  }
+  for (int64_t m = 0; m < pl->A; ++m) {
+    int32_t a = pl->anchors[m], lo = pl->cu[seq_of(a)];
+    for (int32_t b = pl->cu_branch[m]; b < pl->cu_branch[m + 1]; ++b) {
+      row_lo[Nq + b] = lo;
+      row_hi[Nq + b] = a;
+    }
+  }
+  // Pair counts per q head.
+  pl->pairs[0] = pl->pairs[1] = pl->pairs[2] = 0;
+  for (int64_t i = 0; i < Nq; ++i) pl->pairs[0] += (int64_t)row_hi[i] - row_lo[i] + 1;
+  for (int64_t b = 0; b < Rb; ++b) pl->pairs[1] += (int64_t)row_hi[Nq + b] - row_lo[Nq + b] + 1;
+  for (int64_t m = 0; m < pl->A; ++m) {
+    int64_t L = pl->cu_branch[m + 1] - pl->cu_branch[m];
+    pl->pairs[2] += pl->mode[m] == BA_BLOCK ? L * L : L * (L + 1) / 2;
+  }
+
+  // Query tiles: per sequence, rows sorted by prefix end (main row first on a tie).
+  const int RT = std::max(1, kTileRows / pl->G);
+  pl->rows_per_tile = RT;
+  std::vector<QTile> qt;
+  std::vector<int32_t> trow_id, trow_end;
+  std::vector<int32_t> seq_qt_begin(pl->S + 1, 0);
+  int64_t qi = 0, mi = 0;
+  for (int32_t s = 0; s < pl->S; ++s) {
+    seq_qt_begin[s] = (int32_t)qt.size();
+    const int32_t hi_pos = pl->cu[s + 1];
+    std::vector<int32_t> rows;
+    while (qi < Nq || mi < pl->A) {
+      bool take_main = qi < Nq && pl->q_pos[qi] < hi_pos &&
+                       (mi >= pl->A || pl->anchors[mi] >= hi_pos || pl->q_pos[qi] <= pl->anchors[mi]);
+      if (take_main) {
+        rows.push_back((int32_t)qi++);
+      } else if (mi < pl->A && pl->anchors[mi] < hi_pos) {
+        for (int32_t b = pl->cu_branch[mi]; b < pl->cu_branch[mi + 1]; ++b) rows.push_back((int32_t)(Nq + b));
+        ++mi;
+      } else {
+        break;
+      }
+    }
+    for (size_t r0 = 0; r0 < rows.size(); r0 += RT) {
+      size_t n = std::min(rows.size() - r0, (size_t)RT);
+      QTile t{};
+      t.row_begin = (int32_t)trow_id.size();
+      t.nrows = (int32_t)n;
+      t.kv_lo = pl->cu[s];
+      t.end_min = row_hi[rows[r0]];
+      t.end_max = row_hi[rows[r0 + n - 1]];
+      t.seq = s;
+      for (size_t i = 0; i < (size_t)RT; ++i) {
+        bool ok = i < n;
+        trow_id.push_back(ok ? rows[r0 + i] : -1);
+        trow_end.push_back(ok ? row_hi[rows[r0 + i]] : -1);
+      }
+      qt.push_back(t);
+    }
+  }
+  seq_qt_begin[pl->S] = (int32_t)qt.size();
+  pl->n_qtiles = (int32_t)qt.size();
+
+  std::vector<int32_t> fwd_order(qt.size());
+  std::iota(fwd_order.begin(), fwd_order.end(), 0);
+  std::stable_sort(fwd_order.begin(), fwd_order.end(), [&](int32_t a, int32_t b) {
+    int64_t ca = (int64_t)(qt[a].end_max - qt[a].kv_lo + 1) * qt[a].nrows;
+    int64_t cb = (int64_t)(qt[b].end_max - qt[b].kv_lo + 1) * qt[b].nrows;
+    return ca > cb;
+  });
+
+  // Backward key tiles: per sequence, kBwdKeys main keys each; the query tiles
+  // that see a key tile are the sequence's tiles whose largest end reaches it.
+  std::vector<KTile> kt;
+  std::vector<int64_t> kt_cost;
+  std::vector<int64_t> rows_prefix(qt.size() + 1, 0);
+  for (size_t i = 0; i < qt.size(); ++i) rows_prefix[i + 1] = rows_prefix[i] + qt[i].nrows;
+  for (int32_t s = 0; s < pl->S; ++s) {
+    int32_t b0 = seq_qt_begin[s], b1 = seq_qt_begin[s + 1];
+    for (int32_t k0 = pl->cu[s]; k0 < pl->cu[s + 1]; k0 += kBwdKeys) {
+      KTile t{};
+      t.key_lo = k0;
+      t.key_hi = std::min(k0 + kBwdKeys, pl->cu[s + 1]);
+      int32_t lo = b0, hi = b1;  // first tile with end_max >= k0
+      while (lo < hi) {
+        int32_t mid = (lo + hi) / 2;
+        if (qt[mid].end_max >= k0) hi = mid; else lo = mid + 1;
+      }
+      t.qt_begin = lo;
+      t.qt_end = b1;
+      kt.push_back(t);
+      kt_cost.push_back(rows_prefix[b1] - rows_prefix[lo]);
+    }
+  }
+  pl->n_ktiles = (int32_t)kt.size();
+  std::vector<int32_t> bwd_order(kt.size());
+  std::iota(bwd_order.begin(), bwd_order.end(), 0);
+  std::stable_sort(bwd_order.begin(), bwd_order.end(),
+                   [&](int32_t a, int32_t b) { return kt_cost[a] > kt_cost[b]; });
+
+  // Device metadata blob.
+  std::vector<int32_t> mode32(pl->mode.begin(), pl->mode.end());
+  std::vector<uint8_t> &blob = pl->blob;
+  blob.clear();
+  size_t cur = 0;
+  BlobLayout &L = pl->layout;
+  L.group_heads = put(blob, cur, pl->group_heads);
+  L.qtiles = put(blob, cur, qt);
+  L.fwd_order = put(blob, cur, fwd_order);
+  L.tile_row_id = put(blob, cur, trow_id);
+  L.tile_row_end = put(blob, cur, trow_end);
+  L.row_lo = put(blob, cur, row_lo);
+  L.row_hi = put(blob, cur, row_hi);
+  L.cu_branch = put(blob, cur, pl->cu_branch);
+  L.mode = put(blob, cur, mode32);
+  L.ktiles = put(blob, cur, kt);
+  L.bwd_order = put(blob, cur, bwd_order);
+  L.total = cur;
+  blob.resize(std::max<size_t>(cur, 256));
+
+  // Workspace layouts.
+  const size_t f32 = sizeof(float);
+  size_t base = align_up(blob.size(), 256);
+  pl->ws_split = base;
+  size_t o_bytes = align_up((size_t)Rb * pl->hq * pl->d * f32, 256);
+  size_t l_bytes = align_up((size_t)Rb * pl->hq * f32, 256);
+  pl->off_o_pre = base;
+  pl->off_lse_pre = pl->off_o_pre + o_bytes;
+  pl->off_o_loc = pl->off_lse_pre + l_bytes;
+  pl->off_lse_loc = pl->off_o_loc + o_bytes;
+  pl->ws_fwd = pl->off_lse_loc + l_bytes;
+  pl->off_delta = base;
+  size_t d_bytes = align_up((size_t)R * pl->hq * f32, 256);
+  pl->off_dq_acc = pl->off_delta + d_bytes;
+  pl->ws_bwd = pl->off_dq_acc + align_up((size_t)R * pl->hq * pl->d * f32, 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+ba_status_t ba_plan_create(const ba_problem_t *problem, ba_plan_t **out) {
+  if (!out) return set_error(BA_EINVAL, "out is NULL");
+  *out = nullptr;
+  ba_plan *pl = new (std::nothrow) ba_plan();
+  if (!pl) return set_error(BA_EINVAL, "out of host memory");
+  ba_status_t st;
+  try {
+    st = validate_and_copy(problem, pl);
+    if (st == BA_OK) build(pl);
+  } catch (const std::bad_alloc &) {
+    st = set_error(BA_EINVAL, "out of host memory while building the plan");
+  }
+  if (st != BA_OK) {
+    delete pl;
+    return st;
+  }
+  *out = pl;
+  return BA_OK;
+}
+
+void ba_plan_destroy(ba_plan_t *plan) { delete plan; }
+
+size_t ba_workspace_bytes(const ba_plan_t *plan, int pass) {
+  if (!plan) return 0;
+  switch (pass) {
+    case 0: return plan->ws_fwd;
+    case 1: return plan->ws_bwd;
+    case 2: return plan->ws_split;
+    default: return 0;
+  }
+}
+
+ba_status_t ba_plan_sizes(const ba_plan_t *plan, int64_t out[5]) {
+  if (!plan || !out) return set_error(BA_EINVAL, "NULL argument");
+  out[0] = plan->N;
+  out[1] = plan->Nq;
+  out[2] = plan->Rb;
+  out[3] = plan->n_qtiles;
+  out[4] = plan->n_ktiles;
+  return BA_OK;
+}
+
+ba_status_t ba_plan_pairs(const ba_plan_t *plan, int64_t out[3]) {
+  if (!plan || !out) return set_error(BA_EINVAL, "NULL argument");
+  for (int i = 0; i < 3; ++i) out[i] = plan->pairs[i];
+  return BA_OK;
+}
+
+const char *ba_status_str(ba_status_t st) {
+  switch (st) {
+    case BA_OK: return "BA_OK";
+    case BA_EINVAL: return "BA_EINVAL";
+    case BA_EUNSUPPORTED: return "BA_EUNSUPPORTED";
+    case BA_EWORKSPACE: return "BA_EWORKSPACE";
+    case BA_EHIP: return "BA_EHIP";
+  }
+  return "unknown status";
+}
+
+const char *ba_last_error(void) { return ba::last_error(); }
+
+int ba_abi_version(void) { return BA_ABI_VERSION; }
+
+}  // extern "C"

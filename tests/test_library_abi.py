@@ -1,0 +1,112 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/branch_attn.h
+declares, validates problems with the documented statuses, and its plan agrees
+with the oracle on visible-pair counts (no GPU needed: planning is host code)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads as W
+from workloads.configs import custom, TTT, BLOCK
+
+sda = pytest.importorskip("speculative_draft_branch_amd")
+from speculative_draft_branch_amd import Plan, BranchAttnError, BA_EINVAL, BA_EUNSUPPORTED, BA_BF16, BA_F32  # noqa
+
+import oracle
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "branch_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\(", text)
+    skip = {"if", "sizeof", "defined", "extern", "typedef"}
+    return sorted({n for n in names if n not in skip and (n.startswith("ba_") or n in (
+        "branch_attn_fwd", "branch_attn_bwd", "lse_merge"))})
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(sda.library_path())
+    declared = _declared_functions()
+    assert "branch_attn_fwd" in declared and "lse_merge" in declared and "ba_plan_create" in declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(sda.exported_symbols())
+    assert sda.abi_version() == 1
+
+
+def _plan(**kw):
+    base = dict(dtype=BA_BF16, num_q_heads=4, num_kv_heads=2, head_dim=128, cu_seqlens=[0, 5, 9],
+                q_pos=None, anchors=[1, 6], cu_branch=[0, 2, 5], modes=[TTT, BLOCK])
+    base.update(kw)
+    return Plan(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=6, num_kv_heads=4), BA_EINVAL),
+    (dict(head_dim=96), BA_EUNSUPPORTED),
+    (dict(cu_seqlens=[1, 5, 9]), BA_EINVAL),
+    (dict(cu_seqlens=[0, 5, 4]), BA_EINVAL),
+    (dict(q_pos=[0, 3, 3]), BA_EINVAL),
+    (dict(q_pos=[0, 9]), BA_EINVAL),
+    (dict(anchors=[6, 1]), BA_EINVAL),
+    (dict(anchors=[1, 9]), BA_EINVAL),
+    (dict(cu_branch=[0, 3, 2]), BA_EINVAL),
+    (dict(cu_branch=[1, 2, 5]), BA_EINVAL),
+    (dict(cu_branch=[0, 2, 40]), BA_EINVAL),
+    (dict(modes=[TTT, 7]), BA_EINVAL),
+    (dict(kv_head_of=[0, 0, 0, 1]), BA_EINVAL),
+    (dict(kv_head_of=[0, 1, 2, 1]), BA_EINVAL),
+    (dict(dtype=5), BA_EINVAL),
+])
+def test_plan_rejects_malformed_problems(kw, status):
+    with pytest.raises(BranchAttnError) as e:
+        _plan(**kw)
+    assert e.value.status == status
+
+
+def test_plan_accepts_edge_cases():
+    # no branches, single-token sequences, empty sequences, a strided kv_head_of map
+    p = _plan(anchors=[], cu_branch=[0], modes=[])
+    assert p.Rb == 0 and p.Nq == 9
+    p = _plan(cu_seqlens=[0, 1, 1, 2, 9], anchors=[0, 1], cu_branch=[0, 1, 3], modes=[TTT, BLOCK])
+    assert p.N == 9 and p.Rb == 3
+    p = _plan(kv_head_of=[0, 1, 0, 1])
+    assert p.Nq == 9
+    p = _plan(q_pos=[], anchors=[4], cu_branch=[0, 3], modes=[TTT])
+    assert p.Nq == 0 and p.Rb == 3
+
+
+def _pairs_oracle(w):
+    c = oracle.pair_counts(oracle.Problem.from_workload(w))
+    return (c["main"], c["branch_prefix"], c["branch_local"])
+
+
+@pytest.mark.parametrize("name", W.names())
+def test_plan_pair_counts_match_oracle(name):
+    w = W.get(name)
+    p = Plan.from_workload(w)
+    assert p.pairs == _pairs_oracle(w)
+    assert (p.N, p.Nq, p.Rb) == (w.N, w.Nq, w.Rb)
+    # every row lands in exactly one query tile; each tile covers <= 128 MFMA rows
+    G = w.num_q_heads // w.num_kv_heads
+    rt = max(1, 128 // G)
+    assert p.n_qtiles >= -(-(w.Nq + w.Rb) // rt)
+
+
+def test_plan_pair_counts_tiny_cases():
+    w = custom("t", "bf16", 4, 2, 64, [5, 7, 4], [1, 4, 5, 9, 13, 15], [0, 2, 5, 6, 11, 12, 15],
+               [2, 3, 1, 4, 3, 0, 2], [TTT, BLOCK, TTT, BLOCK, TTT, TTT, BLOCK])
+    assert Plan.from_workload(w).pairs == _pairs_oracle(w)
+
+
+def test_workspace_sizes_cover_partials():
+    w = W.get("ctx256k_rank3_chunk64")
+    p = Plan.from_workload(w)
+    f32 = 4
+    assert p.workspace_bytes(0) >= 2 * w.Rb * w.num_q_heads * w.head_dim * f32
+    assert p.workspace_bytes(1) >= (w.Nq + w.Rb) * w.num_q_heads * (w.head_dim + 1) * f32
+    assert 0 < p.workspace_bytes(2) <= p.workspace_bytes(0)

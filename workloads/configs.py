@@ -194,7 +194,7 @@ _REGISTRY: Dict[str, Callable[[], Workload]] = {
     "dflash_64k_1024": lambda: dflash_64k(1024),
     "ctx256k_rank3_chunk64": lambda: ctx256k_rank3(64),
     "ctx256k_rank3_chunk80": lambda: ctx256k_rank3(80),
-    "gptoss_128k_mixed_4096": lambda: gptoss_128k_mixed(4096, 64, 1024, 0),
+    "gptoss_128k_mixed_2048": lambda: gptoss_128k_mixed(2048, 32, 512, 0),
 }
 
 

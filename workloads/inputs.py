@@ -1,7 +1,9 @@
 """Seeded input tensors for a workload.
 
-Tensors are drawn from ``numpy.random.default_rng(seed)`` as float32 normals in
-the fixed order Q, K, V, Qb, Kb, Vb, dO, dOb, scaled by the workload's std.
+Tensors are float32 normals scaled by the workload's std. Tensor t of the fixed
+order Q, K, V, Qb, Kb, Vb, dO, dOb is cut into chunks of 2^22 elements; chunk c
+is drawn from its own generator, ``default_rng(SeedSequence([seed, t, c]))``, so
+chunks can be drawn in parallel and the values do not depend on the thread count.
 bf16 workloads round them to bf16 with round-to-nearest-even and keep the raw
 16-bit patterns (``uint16``); the float32 view of those patterns is exact, so
 the oracle and the GPU see bit-identical values.
@@ -12,13 +14,16 @@ Layouts (row-major, head_dim contiguous):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
 from typing import Dict
 
 import numpy as np
 
 from .configs import Workload
 
-_CHUNK = 1 << 24  # elements generated per call, bounds host memory for the large workloads
+_CHUNK = 1 << 22  # elements per independently seeded chunk
+_ORDER = ["q", "k", "v", "qb", "kb", "vb", "do", "dob"]
 
 
 def bf16_round_bits(x: np.ndarray) -> np.ndarray:
@@ -42,27 +47,32 @@ def shapes(w: Workload) -> Dict[str, tuple]:
     }
 
 
-def _draw(rng: np.random.Generator, shape: tuple, std: float, dtype: str) -> np.ndarray:
+def _draw(seed: int, tidx: int, shape: tuple, std: float, dtype: str, pool) -> np.ndarray:
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint16 if dtype == "bf16" else np.float32)
-    for lo in range(0, n, _CHUNK):
-        hi = min(n, lo + _CHUNK)
+
+    def one(c):
+        lo, hi = c * _CHUNK, min(n, (c + 1) * _CHUNK)
+        rng = np.random.default_rng(np.random.SeedSequence([seed, tidx, c]))
         x = rng.standard_normal(hi - lo, dtype=np.float32)
         if std != 1.0:
             x *= np.float32(std)
         out[lo:hi] = bf16_round_bits(x) if dtype == "bf16" else x
+
+    list(pool.map(one, range((n + _CHUNK - 1) // _CHUNK)))
     return out.reshape(shape)
 
 
-def make_inputs(w: Workload, grads: bool = False) -> Dict[str, np.ndarray]:
+def make_inputs(w: Workload, grads: bool = False, threads: int = 0) -> Dict[str, np.ndarray]:
     """Seeded tensors for ``w``: bf16 bit patterns (uint16) or float32 arrays."""
-    rng = np.random.default_rng(w.seed)
     sh = shapes(w)
-    names = ["q", "k", "v", "qb", "kb", "vb"] + (["do", "dob"] if grads else [])
+    names = _ORDER if grads else _ORDER[:6]
+    threads = threads or min(16, len(os.sched_getaffinity(0)))
     out = {}
-    for nm in names:
-        std = w.grad_std if nm in ("do", "dob") else w.std
-        out[nm] = _draw(rng, sh[nm], std, w.dtype)
+    with cf.ThreadPoolExecutor(max_workers=threads) as pool:
+        for nm in names:
+            std = w.grad_std if nm in ("do", "dob") else w.std
+            out[nm] = _draw(w.seed, _ORDER.index(nm), sh[nm], std, w.dtype, pool)
     return out
 
 
