@@ -43,7 +43,8 @@ def kernel_source_hash(names):
 
 
 KERNEL_SOURCES = {"main_fwd": ["main_fwd.hip", "common.hpp", "plan.hpp"],
-                  "main_bwd": ["main_bwd.hip", "common.hpp", "plan.hpp"]}
+                  "main_bwd_dq": ["main_bwd.hip", "common.hpp", "plan.hpp"],
+                  "main_bwd_dkdv": ["main_bwd.hip", "common.hpp", "plan.hpp"]}
 
 
 def traffic_from_profile(kernel, workload):
@@ -194,7 +195,11 @@ def main():
     fwd_ms = sum(kern[k][0] for k in ("metadata_upload", "main_fwd", "branch_local_fwd", "lse_merge")) / args.steps
     bwd_ms = ms - fwd_ms
     main_pairs = plan.pairs[0] + plan.pairs[1]
-    algo = {"main_fwd": 4 * d * hq * main_pairs, "main_bwd": 10 * d * hq * main_pairs}
+    # contraction flops each kernel must do per visible (row, key) pair and q head:
+    # forward QK^T + PV (4d); dq kernel QK^T, dO V^T, dS K (6d); dkdv kernel
+    # QK^T, dO V^T, P^T dO, dS^T Q (8d)
+    algo = {"main_fwd": 4 * d * hq * main_pairs, "main_bwd_dq": 6 * d * hq * main_pairs,
+            "main_bwd_dkdv": 8 * d * hq * main_pairs}
     dominant = max(algo, key=lambda k: kern[k][0])
     dom_ms = kern[dominant][0] / max(1, kern[dominant][1])
     achieved = algo[dominant] / (dom_ms * 1e-3) / 1e12

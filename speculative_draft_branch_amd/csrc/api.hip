@@ -14,11 +14,11 @@ namespace {
 // ---------------------------------------------------------------------------
 // Opt-in per-kernel timing: HIP events recorded on the launch stream.
 enum KernelId {
-  K_UPLOAD = 0, K_MAIN_FWD, K_BRANCH_LOCAL_FWD, K_LSE_MERGE, K_BWD_PREPROCESS, K_DQ_CLEAR, K_MAIN_BWD,
+  K_UPLOAD = 0, K_MAIN_FWD, K_BRANCH_LOCAL_FWD, K_LSE_MERGE, K_BWD_PREPROCESS, K_MAIN_BWD_DQ, K_MAIN_BWD_DKDV,
   K_BRANCH_LOCAL_BWD, K_DQ_CONVERT, K_COUNT
 };
 const char *kKernelNames[K_COUNT] = {"metadata_upload", "main_fwd", "branch_local_fwd", "lse_merge",
-                                     "bwd_preprocess", "dq_clear", "main_bwd", "branch_local_bwd",
+                                     "bwd_preprocess", "main_bwd_dq", "main_bwd_dkdv", "branch_local_bwd",
                                      "dq_convert"};
 
 struct TimingState {
@@ -296,18 +296,28 @@ ba_status_t branch_attn_bwd(const ba_plan_t *pl, const void *q, const void *k, c
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   float *delta = reinterpret_cast<float *>(ws + pl->off_delta);
   float *dq_acc = reinterpret_cast<float *>(ws + pl->off_dq_acc);
-  const int64_t R = pl->Nq + pl->Rb;
-  BA_TRY(timed(K_BWD_PREPROCESS, st, "backward preprocess",
-               [&] { return launch_bwd_preprocess(mt, pl->dtype, o, d_o, ob, d_ob, delta, st); }));
   if (pl->dtype == BA_BF16) {
-    BA_TRY(timed(K_DQ_CLEAR, st, "dq accumulator clear", [&] { return launch_fill_f32(dq_acc, R * hd, 0.0f, st); }));
-    BA_TRY(timed(K_MAIN_BWD, st, "main-sequence backward", [&] {
-      return launch_main_bwd_bf16(mt, (const bf16 *)q, (const bf16 *)qb, (const bf16 *)k, (const bf16 *)v,
-                                  (const bf16 *)d_o, (const bf16 *)d_ob, lse, lseb, delta, dq_acc, (bf16 *)dk,
-                                  (bf16 *)dv, st);
+    bf16 *qt = reinterpret_cast<bf16 *>(ws + pl->off_qt);
+    bf16 *dot = reinterpret_cast<bf16 *>(ws + pl->off_dot);
+    float *lt = reinterpret_cast<float *>(ws + pl->off_lt);
+    float *dtt = reinterpret_cast<float *>(ws + pl->off_dt);
+    int *et = reinterpret_cast<int *>(ws + pl->off_et);
+    BA_TRY(timed(K_BWD_PREPROCESS, st, "backward preprocess", [&] {
+      return launch_bwd_gather_bf16(mt, (const bf16 *)q, (const bf16 *)qb, (const bf16 *)o, (const bf16 *)ob,
+                                    (const bf16 *)d_o, (const bf16 *)d_ob, lse, lseb, delta, qt, dot, lt, dtt, et, st);
+    }));
+    BA_TRY(timed(K_MAIN_BWD_DQ, st, "main-sequence backward (dq)", [&] {
+      return launch_main_bwd_dq_bf16(mt, (const bf16 *)q, (const bf16 *)qb, (const bf16 *)k, (const bf16 *)v,
+                                     (const bf16 *)d_o, (const bf16 *)d_ob, lse, lseb, delta, dq_acc, st);
+    }));
+    BA_TRY(timed(K_MAIN_BWD_DKDV, st, "main-sequence backward (dk, dv)", [&] {
+      return launch_main_bwd_dkdv_bf16(mt, (const bf16 *)k, (const bf16 *)v, qt, dot, lt, dtt, et, (bf16 *)dk,
+                                       (bf16 *)dv, st);
     }));
   } else {
-    BA_TRY(timed(K_MAIN_BWD, st, "main-sequence backward", [&] {
+    BA_TRY(timed(K_BWD_PREPROCESS, st, "backward preprocess",
+                 [&] { return launch_bwd_preprocess(mt, pl->dtype, o, d_o, ob, d_ob, delta, st); }));
+    BA_TRY(timed(K_MAIN_BWD_DKDV, st, "main-sequence backward", [&] {
       return launch_main_bwd_f32(mt, (const float *)q, (const float *)qb, (const float *)k, (const float *)v,
                                  (const float *)d_o, (const float *)d_ob, lse, lseb, delta, dq_acc, (float *)dk,
                                  (float *)dv, st);

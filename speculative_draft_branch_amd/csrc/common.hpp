@@ -44,6 +44,28 @@ template <class T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
+// Tile descriptors are the same for every lane; reading them through
+// readfirstlane keeps tile-level control and addressing in scalar registers.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ QTile load_qtile(const QTile *p) {
+  QTile t = *p;
+  t.row_begin = uni(t.row_begin);
+  t.nrows = uni(t.nrows);
+  t.kv_lo = uni(t.kv_lo);
+  t.end_min = uni(t.end_min);
+  t.end_max = uni(t.end_max);
+  t.seq = uni(t.seq);
+  return t;
+}
+__device__ __forceinline__ KTile load_ktile(const KTile *p) {
+  KTile t = *p;
+  t.key_lo = uni(t.key_lo);
+  t.key_hi = uni(t.key_hi);
+  t.qt_begin = uni(t.qt_begin);
+  t.qt_end = uni(t.qt_end);
+  return t;
+}
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -93,6 +115,64 @@ __device__ __forceinline__ int lds_off(int row, int d) {  // element offset of (
 __device__ __forceinline__ i16x4 lds_read_tr(const bf16 *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
 }
+
+// Stage rows [k0, k0 + ROWS) of a [rows, Hkv, HD] bf16 tensor (kv head g) into
+// an LDS tile in the swizzled layout; rows past `last` (inclusive bound) are
+// zero-filled. All NT threads of the block take part.
+template <int HD, int ROWS, int NT>
+__device__ __forceinline__ void stage_rows(bf16 *lds, const bf16 *__restrict__ src, int hkv, int g, int k0, int last,
+                                           int tid) {
+  constexpr int NCH = HD / 8;
+  static_assert((ROWS * NCH) % NT == 0, "tile must split evenly over the block");
+#pragma unroll
+  for (int it = 0; it < ROWS * NCH / NT; ++it) {
+    const int c = tid + it * NT;
+    const int r = c / NCH, ch = c % NCH;
+    const int key = k0 + r;
+    uint4 x = {0u, 0u, 0u, 0u};
+    if (key <= last) x = *reinterpret_cast<const uint4 *>(src + ((int64_t)key * hkv + g) * HD + ch * 8);
+    *reinterpret_cast<uint4 *>(lds + r * HD + ((ch ^ swz<HD>(r)) << 3)) = x;
+  }
+}
+
+// Asynchronous form of stage_rows: global_load_lds (16 bytes per lane, gfx950)
+// writes each wave's 1 KB block of the swizzled tile straight into LDS, so lane
+// l of block b fetches the logical chunk that the swizzle places at LDS offset
+// b*1KB + 16*l. Rows past `last` are clamped to `last` (callers mask those
+// keys). Completion is tracked by vmcnt: wait_async_loads() then a barrier
+// before the tile is read.
+template <int HD, int ROWS, int NT>
+__device__ __forceinline__ void stage_rows_async(bf16 *lds, const bf16 *__restrict__ src, int hkv, int g, int k0,
+                                                 int last, int tid) {
+  constexpr int NCH = HD / 8;          // 16-byte chunks per row
+  constexpr int RPB = 64 / NCH;        // rows per 1 KB wave block
+  constexpr int BLOCKS = ROWS / RPB;   // 1 KB blocks in the tile
+  static_assert(BLOCKS % (NT / 64) == 0, "tile must split evenly over the waves");
+  constexpr int PER_WAVE = BLOCKS / (NT / 64);
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int it = 0; it < PER_WAVE; ++it) {
+    const int b = wave * PER_WAVE + it;
+    const int r = b * RPB + lane / NCH;
+    const int ch = (lane % NCH) ^ swz<HD>(r);
+    const int key = min(k0 + r, last);
+    const bf16 *gp = src + ((int64_t)key * hkv + g) * HD + ch * 8;
+    __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void *)(lds + b * 512), 16, 0, 0);
+  }
+}
+
+// Asynchronous copy of 64*n consecutive 32-bit words into LDS by one wave
+// (global_load_lds, 4 bytes per lane).
+template <int N>
+__device__ __forceinline__ void stage_words_async(void *lds, const void *__restrict__ src, int lane) {
+#pragma unroll
+  for (int it = 0; it < N; ++it)
+    __builtin_amdgcn_global_load_lds(static_cast<const uint32_t *>(src) + it * 64 + lane,
+                                     (__attribute__((address_space(3))) void *)(static_cast<uint32_t *>(lds) + it * 64),
+                                     4, 0, 0);
+}
+
+__device__ __forceinline__ void wait_async_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ bf16x8 join(i16x4 a, i16x4 b) {
   typedef short i16x8 __attribute__((ext_vector_type(8)));

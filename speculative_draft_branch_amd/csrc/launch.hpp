@@ -27,8 +27,14 @@ hipError_t launch_main_bwd_f32(const Meta &mt, const float *q, const float *qb, 
 // bf16 MFMA main-sequence kernels
 hipError_t launch_main_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *v,
                                 bf16 *o, float *lse, float *o_pre, float *lse_pre, hipStream_t st);
-hipError_t launch_main_bwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *v,
-                                const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
-                                const float *delta, float *dq_acc, bf16 *dk, bf16 *dv, hipStream_t st);
+hipError_t launch_main_bwd_dq_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *v,
+                                   const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
+                                   const float *delta, float *dq_acc, hipStream_t st);
+hipError_t launch_bwd_gather_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *o, const bf16 *ob,
+                                  const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
+                                  float *delta, bf16 *qt, bf16 *dot, float *lt, float *dtt, int *et, hipStream_t st);
+hipError_t launch_main_bwd_dkdv_bf16(const Meta &mt, const bf16 *k, const bf16 *v, const bf16 *qt, const bf16 *dot,
+                                     const float *lt, const float *dtt, const int *et, bf16 *dk, bf16 *dv,
+                                     hipStream_t st);
 
 }  // namespace ba

@@ -2,250 +2,412 @@
 // attention over its causal main prefix, taken through the row's final (merged)
 // LSE, so the log-sum-exp merge needs no backward of its own:
 //   P = exp(S - LSE),  dP = dO V^T,  dS = P * (dP - D),  D = rowsum(dO * O),
-//   dV += P^T dO,  dK += scale dS^T Q,  dQ += scale dS K.
+//   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
 // (Decomposition and merge: evolve.pub review, "Scope & Claims", section 3.2 and
 // Eq. 2; the merged result is one softmax over the union of keys, rcap.io
 // explainer, paragraph on branch attention under context parallelism.)
 //
-// Work unit: 128 main keys of one kv head (one backward key tile) against every
-// query tile whose rows may see them; each of the 4 waves owns 32 keys and keeps
-// their dK/dV in registers across all query tiles, so each key's gradient is
-// written once, summed over the q heads of the group. dQ is accumulated with
-// float32 atomics into a workspace buffer, once per workgroup per query tile,
-// after the waves' dS blocks are exchanged through LDS.
-//
-// MFMA layouts (v_mfma_f32_32x32x16_bf16): S = Q K^T puts the key on the lane
-// (lane % 32) and 16 query rows in the lane's registers, so P and dS are
-// directly the A operand of the dV and dK products; dO and Q enter those
-// products through the transposing LDS read.
+// Two kernels, no atomics:
+//  * dq: query-tile major, the forward's work unit (query tile x its key range,
+//    64-key LDS tiles). S^T = K Q^T and dP^T = V dO^T put one query row on each
+//    lane; dQ^T += K^T dS^T takes K through the transposing LDS read and dS^T
+//    straight from registers. dQ is written once per row (float32, into the
+//    accumulator the branch-local backward adds to).
+//  * dkdv: key-tile major: 128 main keys of one kv head against every query
+//    tile whose rows may see them; each wave owns 32 keys and keeps their dK, dV
+//    in registers across all query tiles, written once, summed over the group's
+//    q heads. S = Q K^T puts the key on the lane, so P and dS are directly the
+//    A operands of dV += P^T dO and dK += dS^T Q (dO and Q via the transposing
+//    LDS read).
 #include <climits>
 
 #include "launch.hpp"
 
 namespace ba {
 
+// ---------------------------------------------------------------------------
+namespace {
+
 template <int HD>
-__global__ __launch_bounds__(256) void main_bwd_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
-                                                            const bf16 *__restrict__ qb,
-                                                            const bf16 *__restrict__ k,
-                                                            const bf16 *__restrict__ v,
-                                                            const bf16 *__restrict__ d_o,
-                                                            const bf16 *__restrict__ d_ob,
-                                                            const float *__restrict__ lse,
-                                                            const float *__restrict__ lseb,
-                                                            const float *__restrict__ delta,
-                                                            float *__restrict__ dq_acc, bf16 *__restrict__ dk,
-                                                            bf16 *__restrict__ dv) {
-  constexpr int BK = kBwdKeys;  // 128 keys per workgroup, 32 per wave
-  constexpr int BM = kTileRows; // 128 MFMA rows per query tile
-  constexpr int NCH = HD / 8;
-  constexpr int KS = HD / 16;
-  constexpr int DT = HD / 32;
-  static_assert(BK == 128 && BM == 128, "tile shape");
-  __shared__ __attribute__((aligned(16))) bf16 sQ[BM * HD];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[BM * HD];
-  __shared__ __attribute__((aligned(16))) bf16 sK[BK * HD];
-  __shared__ __attribute__((aligned(16))) bf16 sdS[BK * BM];  // [key][row], 16-byte chunks swizzled
-  __shared__ __attribute__((aligned(16))) float sL2[BM];  // LSE * log2(e); +inf for padding rows
-  __shared__ __attribute__((aligned(16))) float sD[BM];
-  __shared__ int sEnd[BM];       // prefix end; -1 for padding rows
-  __shared__ int64_t sAcc[BM];   // dq_acc element offset of the row; -1 for padding
+struct DqState {
+  static constexpr int KS = HD / 16;
+  static constexpr int DT = HD / 32;
+  bf16x8 qf[KS], of[KS];
+  f32x16 acc[DT];
+  float l2, dd;
+  int end, wmin;
+  int grp, in_j, in_q, lane;
+};
+
+// One 64-key tile [k0, k0 + 64) of the wave's 32 rows against LDS tiles sK, sV.
+template <int HD>
+__device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const bf16 *sV, int k0, float sl2) {
+  constexpr int KS = DqState<HD>::KS, DT = DqState<HD>::DT;
+  const int lane = st.lane;
+  f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int r = kb * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = r * HD + (((2 * ks + (lane >> 5)) ^ swz<HD>(r)) << 3);
+      s[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(sK + off), st.qf[ks], s[kb]);
+      dp[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(sV + off), st.of[ks], dp[kb]);
+    }
+  }
+  const bool need_mask = k0 + 63 > st.wmin;
+  bf16x8 db[4];  // dS^T operands of the four 16-key k-steps
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float p = fast_exp2(fmaf(s[kb][i], sl2, -st.l2));
+      if (need_mask) {
+        const int key = k0 + kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+        if (key > st.end) p = 0.0f;
+      }
+      db[kb * 2 + (i >> 3)][i & 7] = (bf16)(p * (dp[kb][i] - st.dd));
+    }
+  // dQ^T += K^T dS^T; slot 8*half + 4c + j <-> key 16kk + 8c + 4*half + j.
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int key0 = kk * 16 + 4 * (st.grp >> 1) + st.in_j;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = dt * 32 + (st.grp & 1) * 16 + 4 * st.in_q;
+      const bf16x8 a = join(lds_read_tr(sK + lds_off<HD>(key0, d)), lds_read_tr(sK + lds_off<HD>(key0 + 8, d)));
+      st.acc[dt] = mfma32(a, db[kk], st.acc[dt]);
+    }
+  }
+}
+
+}  // namespace
+
+template <int HD>
+__global__ __launch_bounds__(256) void main_bwd_dq_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
+                                                               const bf16 *__restrict__ qb,
+                                                               const bf16 *__restrict__ k,
+                                                               const bf16 *__restrict__ v,
+                                                               const bf16 *__restrict__ d_o,
+                                                               const bf16 *__restrict__ d_ob,
+                                                               const float *__restrict__ lse,
+                                                               const float *__restrict__ lseb,
+                                                               const float *__restrict__ delta,
+                                                               float *__restrict__ dq_acc) {
+  constexpr int BN = 64;
+  constexpr int KS = HD / 16, DT = HD / 32;
+  __shared__ __attribute__((aligned(16))) bf16 sK0[BN * HD];
+  __shared__ __attribute__((aligned(16))) bf16 sV0[BN * HD];
+  __shared__ __attribute__((aligned(16))) bf16 sK1[BN * HD];
+  __shared__ __attribute__((aligned(16))) bf16 sV1[BN * HD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hkv = mt.hkv, G = mt.G;
   const int g = blockIdx.x % hkv;
-  const KTile kt = mt.ktiles[mt.bwd_order[blockIdx.x / hkv]];
+  const QTile tile = load_qtile(mt.qtiles + uni(mt.fwd_order[blockIdx.x / hkv]));
   const int64_t R = mt.Nq + mt.Rb;
+  const int kv_lo = tile.kv_lo, kv_end = tile.end_max;
+  const int ntiles = (kv_end - kv_lo + BN) / BN;
+  stage_rows_async<HD, BN, 256>(sK0, k, hkv, g, kv_lo, kv_end, tid);
+  stage_rows_async<HD, BN, 256>(sV0, v, hkv, g, kv_lo, kv_end, tid);
+
+  DqState<HD> st;
+  const int mrow = wave * 32 + (lane & 31);
+  const int bi = mrow / G, hj = mrow - bi * G;
+  int row = -1;
+  st.end = -1;
+  if (bi < tile.nrows) {
+    row = mt.tile_row_id[tile.row_begin + bi];
+    st.end = mt.tile_row_end[tile.row_begin + bi];
+  }
+  const int h = mt.group_heads[g * G + hj];
+  const bool is_main = row >= 0 && row < mt.Nq;
+  const int64_t roff = row < 0 ? 0
+                       : is_main ? ((int64_t)row * mt.hq + h) * HD
+                                 : ((int64_t)(row - mt.Nq) * mt.hq + h) * HD;
+  {
+    const bf16 *qp = (is_main ? q : qb) + roff + 8 * (lane >> 5);
+    const bf16 *op = (is_main ? d_o : d_ob) + roff + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (row >= 0) {
+        st.qf[ks] = *reinterpret_cast<const bf16x8 *>(qp + 16 * ks);
+        st.of[ks] = *reinterpret_cast<const bf16x8 *>(op + 16 * ks);
+      } else {
+        st.qf[ks] = bf16x8{};
+        st.of[ks] = bf16x8{};
+      }
+    }
+  }
+  st.l2 = INFINITY;  // padding rows: P = 0
+  st.dd = 0.0f;
+  if (row >= 0) {
+    st.l2 = (is_main ? lse[(int64_t)h * mt.Nq + row] : lseb[(int64_t)h * mt.Rb + (row - mt.Nq)]) * kLog2e;
+    st.dd = delta[(int64_t)h * R + row];
+  }
+  st.wmin = wave_min(row >= 0 ? st.end : INT_MAX);
+  const int wmax = wave_max(st.end);
+  const float sl2 = mt.scale * kLog2e;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) st.acc[dt] = f32x16{};
+  st.lane = lane;
+  st.grp = lane >> 4;
+  st.in_j = (lane & 15) >> 2;
+  st.in_q = lane & 3;
+
+  for (int j = 0; j < ntiles; j += 2) {
+    const int k0 = kv_lo + j * BN;
+    wait_async_loads();
+    __syncthreads();  // tile j is in buffer 0; every wave is done with buffer 1
+    if (j + 1 < ntiles) {
+      stage_rows_async<HD, BN, 256>(sK1, k, hkv, g, k0 + BN, kv_end, tid);
+      stage_rows_async<HD, BN, 256>(sV1, v, hkv, g, k0 + BN, kv_end, tid);
+    }
+    if (k0 <= wmax) dq_tile<HD>(st, sK0, sV0, k0, sl2);
+    if (j + 1 >= ntiles) break;
+    wait_async_loads();
+    __syncthreads();  // tile j+1 is in buffer 1; every wave is done with buffer 0
+    if (j + 2 < ntiles) {
+      stage_rows_async<HD, BN, 256>(sK0, k, hkv, g, k0 + 2 * BN, kv_end, tid);
+      stage_rows_async<HD, BN, 256>(sV0, v, hkv, g, k0 + 2 * BN, kv_end, tid);
+    }
+    if (k0 + BN <= wmax) dq_tile<HD>(st, sK1, sV1, k0 + BN, sl2);
+  }
+  if (row >= 0) {
+    float *dst = dq_acc + ((int64_t)row * mt.hq + h) * HD;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = dt * 32 + q4 * 8 + (lane >> 5) * 4;
+        const f32x4 val = {mt.scale * st.acc[dt][q4 * 4 + 0], mt.scale * st.acc[dt][q4 * 4 + 1],
+                           mt.scale * st.acc[dt][q4 * 4 + 2], mt.scale * st.acc[dt][q4 * 4 + 3]};
+        *reinterpret_cast<f32x4 *>(dst + d) = val;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward preprocess for the bf16 path, one workgroup per (query tile, kv
+// head): the tile's 128 MFMA rows in order -- Q and dO rows, LSE * log2(e),
+// D = rowsum(dO * O) -- plus (kv head 0) each row's prefix end, so the
+// key-tile-major kernel streams contiguous 32 KB blocks. Also writes D in the
+// [Hq, rows] layout for the dq and branch-local kernels. Every (row, q head)
+// lies in exactly one (query tile, kv head).
+template <int HD>
+__global__ __launch_bounds__(256) void bwd_gather_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
+                                                              const bf16 *__restrict__ qb,
+                                                              const bf16 *__restrict__ o,
+                                                              const bf16 *__restrict__ ob,
+                                                              const bf16 *__restrict__ d_o,
+                                                              const bf16 *__restrict__ d_ob,
+                                                              const float *__restrict__ lse,
+                                                              const float *__restrict__ lseb,
+                                                              float *__restrict__ delta, bf16 *__restrict__ qt,
+                                                              bf16 *__restrict__ dot, float *__restrict__ lt,
+                                                              float *__restrict__ dtt, int *__restrict__ et) {
+  constexpr int NCH = HD / 8;
+  const int hkv = mt.hkv, G = mt.G;
+  const int g = blockIdx.x % hkv;
+  const int qi = blockIdx.x / hkv;
+  const QTile tile = load_qtile(mt.qtiles + qi);
+  const int m = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int bi = m / G, hj = m - bi * G;
+  const int64_t trow = ((int64_t)qi * hkv + g) * kTileRows + m;
+  uint4 *qd = reinterpret_cast<uint4 *>(qt + trow * HD);
+  uint4 *od = reinterpret_cast<uint4 *>(dot + trow * HD);
+  const bool ok = bi < tile.nrows;
+  float dsum = 0.0f;
+  int row = 0, h = 0;
+  bool is_main = false;
+  if (ok) {
+    row = mt.tile_row_id[tile.row_begin + bi];
+    h = mt.group_heads[g * G + hj];
+    is_main = row < mt.Nq;
+    const int64_t off = is_main ? ((int64_t)row * mt.hq + h) * HD : ((int64_t)(row - mt.Nq) * mt.hq + h) * HD;
+    const uint4 *qs = reinterpret_cast<const uint4 *>((is_main ? q : qb) + off);
+    const uint4 *ds = reinterpret_cast<const uint4 *>((is_main ? d_o : d_ob) + off);
+    const uint4 *os = reinterpret_cast<const uint4 *>((is_main ? o : ob) + off);
+#pragma unroll
+    for (int c = 0; c < NCH / 2; ++c) {
+      const int ch = half * (NCH / 2) + c;
+      qd[ch] = qs[ch];
+      const uint4 y = ds[ch];
+      od[ch] = y;
+      const bf16x8 yb = __builtin_bit_cast(bf16x8, y);
+      const bf16x8 zb = __builtin_bit_cast(bf16x8, os[ch]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = fmaf((float)yb[e], (float)zb[e], dsum);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCH / 2; ++c) {
+      const int ch = half * (NCH / 2) + c;
+      qd[ch] = uint4{0u, 0u, 0u, 0u};
+      od[ch] = uint4{0u, 0u, 0u, 0u};
+    }
+  }
+  dsum += __shfl_xor(dsum, 1, 64);
+  if (half == 0) {
+    if (ok) {
+      const float l = is_main ? lse[(int64_t)h * mt.Nq + row] : lseb[(int64_t)h * mt.Rb + (row - mt.Nq)];
+      lt[trow] = l * kLog2e;
+      dtt[trow] = dsum;
+      delta[(int64_t)h * (mt.Nq + mt.Rb) + row] = dsum;
+    } else {
+      lt[trow] = INFINITY;
+      dtt[trow] = 0.0f;
+    }
+    if (g == 0) et[(int64_t)qi * kTileMetaWords + m] = ok ? mt.tile_row_end[tile.row_begin + bi] : -1;
+  }
+  if (g == 0 && threadIdx.x < kTileMetaWords - kTileRows) {
+    const int w = threadIdx.x;
+    et[(int64_t)qi * kTileMetaWords + kTileRows + w] =
+        w == 0 ? tile.end_min : w == 1 ? tile.end_max : w == 2 ? tile.nrows * G : 0;
+  }
+}
+
+namespace {
+
+template <int HD>
+struct DkdvState {
+  static constexpr int KS = HD / 16;
+  static constexpr int DT = HD / 32;
+  bf16x8 kf[KS], vf[KS];
+  f32x16 adk[DT], adv[DT];
+  int my_key, wkey_lo, key_hi;
+  int grp, in_j, in_q, lane;
+};
+
+// One query tile (128 MFMA rows staged in LDS) against the wave's 32 keys.
+template <int HD>
+__device__ __forceinline__ void dkdv_tile(DkdvState<HD> &st, const bf16 *sQ, const bf16 *sdO, const float *sL2,
+                                          const float *sD, const int *sEnd, float sl2) {
+  constexpr int BM = kTileRows;
+  constexpr int KS = DkdvState<HD>::KS, DT = DkdvState<HD>::DT;
+  const int lane = st.lane;
+  const int end_min = uni(sEnd[BM]), end_max = uni(sEnd[BM + 1]), valid_rows = uni(sEnd[BM + 2]);
+  if (end_max < st.wkey_lo || st.wkey_lo >= st.key_hi) return;  // no row of this tile sees the wave's keys
+  const bool need_mask = end_min < st.wkey_lo + 31 || st.wkey_lo + 31 >= st.key_hi || valid_rows < BM;
+#pragma unroll
+  for (int rb = 0; rb < BM / 32; ++rb) {
+    // S and dP for rows 32rb..32rb+31 x the wave's 32 keys.
+    f32x16 s = f32x16{}, dp = f32x16{};
+    const int ar = rb * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = ar * HD + (((2 * ks + (lane >> 5)) ^ swz<HD>(ar)) << 3);
+      s = mfma32(*reinterpret_cast<const bf16x8 *>(sQ + off), st.kf[ks], s);
+      dp = mfma32(*reinterpret_cast<const bf16x8 *>(sdO + off), st.vf[ks], dp);
+    }
+    // element i: row rb*32 + (i/4)*8 + 4*(lane/32) + i%4, key my_key
+    bf16x8 pa[2], dsa[2];
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int r0 = rb * 32 + i4 * 8 + 4 * (lane >> 5);
+      const f32x4 l2 = *reinterpret_cast<const f32x4 *>(sL2 + r0);
+      const f32x4 dd = *reinterpret_cast<const f32x4 *>(sD + r0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i4 * 4 + e;
+        float p = fast_exp2(fmaf(s[i], sl2, -l2[e]));
+        if (need_mask && (sEnd[r0 + e] < st.my_key || st.my_key >= st.key_hi)) p = 0.0f;
+        pa[i >> 3][i & 7] = (bf16)p;
+        dsa[i >> 3][i & 7] = (bf16)(p * (dp[i] - dd[e]));
+      }
+    }
+    // dV += P^T dO, dK += dS^T Q over these 32 rows (two 16-row k-steps).
+    // Operand slot 8*half + 4c + j <-> row 32rb + 16kh + 8c + 4*half + j.
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int row0 = rb * 32 + kh * 16 + 4 * (st.grp >> 1) + st.in_j;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = dt * 32 + (st.grp & 1) * 16 + 4 * st.in_q;
+        const bf16x8 bo = join(lds_read_tr(sdO + lds_off<HD>(row0, d)), lds_read_tr(sdO + lds_off<HD>(row0 + 8, d)));
+        const bf16x8 bq = join(lds_read_tr(sQ + lds_off<HD>(row0, d)), lds_read_tr(sQ + lds_off<HD>(row0 + 8, d)));
+        st.adv[dt] = mfma32(pa[kh], bo, st.adv[dt]);
+        st.adk[dt] = mfma32(dsa[kh], bq, st.adk[dt]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+template <int HD>
+__global__ __launch_bounds__(256) void main_bwd_dkdv_bf16_kernel(Meta mt, const bf16 *__restrict__ k,
+                                                                 const bf16 *__restrict__ v,
+                                                                 const bf16 *__restrict__ qt_rows,
+                                                                 const bf16 *__restrict__ do_rows,
+                                                                 const float *__restrict__ lt,
+                                                                 const float *__restrict__ dtt,
+                                                                 const int *__restrict__ et,
+                                                                 bf16 *__restrict__ dk, bf16 *__restrict__ dv) {
+  constexpr int BM = kTileRows;  // 128 MFMA rows per query tile
+  constexpr int KS = HD / 16, DT = HD / 32;
+  static_assert(kBwdKeys == 128 && BM == 128, "tile shape");
+  __shared__ __attribute__((aligned(16))) bf16 sQ0[BM * HD];
+  __shared__ __attribute__((aligned(16))) bf16 sO0[BM * HD];
+  __shared__ __attribute__((aligned(16))) bf16 sQ1[BM * HD];
+  __shared__ __attribute__((aligned(16))) bf16 sO1[BM * HD];
+  __shared__ __attribute__((aligned(16))) float sL0[BM], sD0[BM], sL1[BM], sD1[BM];
+  __shared__ __attribute__((aligned(16))) int sE0[kTileMetaWords], sE1[kTileMetaWords];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hkv = mt.hkv;
+  const int g = blockIdx.x % hkv;
+  const KTile kt = load_ktile(mt.ktiles + uni(mt.bwd_order[blockIdx.x / hkv]));
   const float sl2 = mt.scale * kLog2e;
 
-  // Stage this workgroup's K tile in LDS (for the dQ product) and keep the
-  // wave's own K and V as MFMA B operands: lane holds key 32*wave + lane%32,
+  // Query tile qi, kv head g -> one LDS buffer (all asynchronous).
+  auto prefetch = [&](int qi, bf16 *sQ, bf16 *sO, float *sL, float *sD, int *sE) {
+    const int64_t tb = ((int64_t)qi * hkv + g) * BM;
+    stage_rows_async<HD, BM, 256>(sQ, qt_rows + tb * HD, 1, 0, 0, BM - 1, tid);
+    stage_rows_async<HD, BM, 256>(sO, do_rows + tb * HD, 1, 0, 0, BM - 1, tid);
+    if (wave == 0) stage_words_async<BM / 64>(sL, lt + tb, lane);
+    else if (wave == 1) stage_words_async<BM / 64>(sD, dtt + tb, lane);
+    else if (wave == 2) stage_words_async<kTileMetaWords / 64>(sE, et + (int64_t)qi * kTileMetaWords, lane);
+  };
+  if (kt.qt_begin < kt.qt_end) prefetch(kt.qt_begin, sQ0, sO0, sL0, sD0, sE0);
+
+  // The wave's own K and V as B operands: lane holds key 32*wave + lane%32,
   // d = 16*ks + 8*(lane/32) + 0..7.
-#pragma unroll
-  for (int it = 0; it < BK * NCH / 256; ++it) {
-    const int c = tid + it * 256;
-    const int r = c / NCH, ch = c % NCH;
-    const int key = kt.key_lo + r;
-    uint4 kx = {0u, 0u, 0u, 0u};
-    if (key < kt.key_hi) kx = *reinterpret_cast<const uint4 *>(k + ((int64_t)key * hkv + g) * HD + ch * 8);
-    *reinterpret_cast<uint4 *>(sK + r * HD + ((ch ^ swz<HD>(r)) << 3)) = kx;
-  }
-  const int my_key = kt.key_lo + wave * 32 + (lane & 31);
-  bf16x8 kf[KS], vf[KS];
+  DkdvState<HD> st;
+  st.my_key = kt.key_lo + wave * 32 + (lane & 31);
+  st.wkey_lo = kt.key_lo + wave * 32;
+  st.key_hi = kt.key_hi;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    if (my_key < kt.key_hi) {
-      const int64_t src = ((int64_t)my_key * hkv + g) * HD + 16 * ks + 8 * (lane >> 5);
-      kf[ks] = *reinterpret_cast<const bf16x8 *>(k + src);
-      vf[ks] = *reinterpret_cast<const bf16x8 *>(v + src);
+    if (st.my_key < kt.key_hi) {
+      const int64_t src = ((int64_t)st.my_key * hkv + g) * HD + 16 * ks + 8 * (lane >> 5);
+      st.kf[ks] = *reinterpret_cast<const bf16x8 *>(k + src);
+      st.vf[ks] = *reinterpret_cast<const bf16x8 *>(v + src);
     } else {
-      kf[ks] = bf16x8{};
-      vf[ks] = bf16x8{};
+      st.kf[ks] = bf16x8{};
+      st.vf[ks] = bf16x8{};
     }
   }
-  const int wkey_lo = kt.key_lo + wave * 32;  // first key of this wave
-
-  f32x16 adk[DT], adv[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    adk[dt] = f32x16{};
-    adv[dt] = f32x16{};
+    st.adk[dt] = f32x16{};
+    st.adv[dt] = f32x16{};
   }
-  const int grp = lane >> 4, in_j = (lane & 15) >> 2, in_q = lane & 3;
+  st.lane = lane;
+  st.grp = lane >> 4;
+  st.in_j = (lane & 15) >> 2;
+  st.in_q = lane & 3;
 
-  for (int qi = kt.qt_begin; qi < kt.qt_end; ++qi) {
-    const QTile qt = mt.qtiles[qi];
-    __syncthreads();  // previous iteration's LDS reads are done
-    {
-      // Two threads per MFMA row: row metadata and half of its Q / dO row each.
-      const int m = tid >> 1, half = tid & 1;
-      const int bi = m / G, hj = m - bi * G;
-      const bool ok = bi < qt.nrows;
-      int row = -1;
-      int64_t qoff = 0;
-      if (ok) {
-        row = mt.tile_row_id[qt.row_begin + bi];
-        const int h = mt.group_heads[g * G + hj];
-        const bool is_main = row < mt.Nq;
-        qoff = is_main ? ((int64_t)row * mt.hq + h) * HD : ((int64_t)(row - mt.Nq) * mt.hq + h) * HD;
-        if (half == 0) {
-          const float l = is_main ? lse[(int64_t)h * mt.Nq + row] : lseb[(int64_t)h * mt.Rb + (row - mt.Nq)];
-          sL2[m] = l * kLog2e;
-          sD[m] = delta[(int64_t)h * R + row];
-          sEnd[m] = mt.tile_row_end[qt.row_begin + bi];
-          sAcc[m] = ((int64_t)row * mt.hq + h) * HD;
-        }
-        const bf16 *qp = (is_main ? q : qb) + qoff;
-        const bf16 *dp = (is_main ? d_o : d_ob) + qoff;
-#pragma unroll
-        for (int c = 0; c < NCH / 2; ++c) {
-          const int ch = half * (NCH / 2) + c;
-          const int dst = m * HD + ((ch ^ swz<HD>(m)) << 3);
-          *reinterpret_cast<uint4 *>(sQ + dst) = *reinterpret_cast<const uint4 *>(qp + ch * 8);
-          *reinterpret_cast<uint4 *>(sdO + dst) = *reinterpret_cast<const uint4 *>(dp + ch * 8);
-        }
-      } else {
-        if (half == 0) {
-          sL2[m] = INFINITY;
-          sD[m] = 0.0f;
-          sEnd[m] = -1;
-          sAcc[m] = -1;
-        }
-#pragma unroll
-        for (int c = 0; c < NCH / 2; ++c) {
-          const int ch = half * (NCH / 2) + c;
-          const int dst = m * HD + ((ch ^ swz<HD>(m)) << 3);
-          *reinterpret_cast<uint4 *>(sQ + dst) = uint4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<uint4 *>(sdO + dst) = uint4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-    __syncthreads();
-
-    // Does any row of this query tile end before one of this wave's keys?
-    const bool need_mask = qt.end_min < wkey_lo + 31 || wkey_lo + 31 >= kt.key_hi || qt.nrows * G < BM;
-    const bool any_visible = qt.end_max >= wkey_lo && wkey_lo < kt.key_hi;
-    if (any_visible) {
-#pragma unroll
-      for (int rb = 0; rb < BM / 32; ++rb) {
-        // S and dP for rows 32rb..32rb+31 x the wave's 32 keys.
-        f32x16 s = f32x16{}, dp = f32x16{};
-        const int ar = rb * 32 + (lane & 31);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int ch = 2 * ks + (lane >> 5);
-          const int off = ar * HD + ((ch ^ swz<HD>(ar)) << 3);
-          s = mfma32(*reinterpret_cast<const bf16x8 *>(sQ + off), kf[ks], s);
-          dp = mfma32(*reinterpret_cast<const bf16x8 *>(sdO + off), vf[ks], dp);
-        }
-        // element i: row rb*32 + (i/4)*8 + 4*(lane/32) + i%4, key my_key
-        bf16x8 pa[2], dsa[2];
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int r0 = rb * 32 + i4 * 8 + 4 * (lane >> 5);
-          const f32x4 l2 = *reinterpret_cast<const f32x4 *>(sL2 + r0);
-          const f32x4 dd = *reinterpret_cast<const f32x4 *>(sD + r0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = i4 * 4 + e;
-            float p = fast_exp2(fmaf(s[i], sl2, -l2[e]));
-            if (need_mask && (sEnd[r0 + e] < my_key || my_key >= kt.key_hi)) p = 0.0f;
-            const float ds = p * (dp[i] - dd[e]);
-            pa[i >> 3][i & 7] = (bf16)p;
-            dsa[i >> 3][i & 7] = (bf16)ds;
-          }
-        }
-        // dV += P^T dO and dK += dS^T Q over these 32 rows (two 16-row k-steps).
-        // Operand slot 8*half + 4c + j <-> row 32rb + 16kh + 8c + 4*half + j.
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const int row0 = rb * 32 + kh * 16 + 4 * (grp >> 1) + in_j;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const int d = dt * 32 + (grp & 1) * 16 + 4 * in_q;
-            const bf16x8 bo = join(lds_read_tr(sdO + lds_off<HD>(row0, d)), lds_read_tr(sdO + lds_off<HD>(row0 + 8, d)));
-            const bf16x8 bq = join(lds_read_tr(sQ + lds_off<HD>(row0, d)), lds_read_tr(sQ + lds_off<HD>(row0 + 8, d)));
-            adv[dt] = mfma32(pa[kh], bo, adv[dt]);
-            adk[dt] = mfma32(dsa[kh], bq, adk[dt]);
-          }
-        }
-        // Stage dS for the dQ product: sdS[key][row], 4 consecutive rows per write.
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int kl = wave * 32 + (lane & 31);
-          const int r0 = rb * 32 + i4 * 8 + 4 * (lane >> 5);
-          const bf16x4 val = {dsa[i4 >> 1][(i4 & 1) * 4 + 0], dsa[i4 >> 1][(i4 & 1) * 4 + 1],
-                              dsa[i4 >> 1][(i4 & 1) * 4 + 2], dsa[i4 >> 1][(i4 & 1) * 4 + 3]};
-          *reinterpret_cast<bf16x4 *>(sdS + lds_off<BM>(kl, r0)) = val;
-        }
-      }
-    } else {
-      // No row of this tile sees the wave's keys: its dS block is zero.
-#pragma unroll
-      for (int rb = 0; rb < BM / 32; ++rb)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int kl = wave * 32 + (lane & 31);
-          const int r0 = rb * 32 + i4 * 8 + 4 * (lane >> 5);
-          *reinterpret_cast<bf16x4 *>(sdS + lds_off<BM>(kl, r0)) = bf16x4{};
-        }
-    }
-    __syncthreads();
-
-    // dQ for rows 32*wave..32*wave+31 against all 128 keys: A = dS (rows x keys)
-    // through the transposing read of sdS, B = K (keys x d) through that of sK.
-    // Slot 8*half + 4c + j <-> key 16*ks + 8*half + 4c + j.
-    // Two passes over halves of head_dim keep the dQ accumulator at DT/2 blocks.
-    constexpr int DH = DT > 1 ? DT / 2 : 1;
-    const int qrow = wave * 32 + (grp & 1) * 16 + 4 * in_q;
-#pragma unroll
-    for (int dpass = 0; dpass < DT / DH; ++dpass) {
-      f32x16 aq[DH];
-#pragma unroll
-      for (int dt = 0; dt < DH; ++dt) aq[dt] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int key0 = ks * 16 + 8 * (grp >> 1) + in_j;
-        const bf16x8 a = join(lds_read_tr(sdS + lds_off<BM>(key0, qrow)), lds_read_tr(sdS + lds_off<BM>(key0 + 4, qrow)));
-#pragma unroll
-        for (int dt = 0; dt < DH; ++dt) {
-          const int d = (dpass * DH + dt) * 32 + (grp & 1) * 16 + 4 * in_q;
-          const bf16x8 b = join(lds_read_tr(sK + lds_off<HD>(key0, d)), lds_read_tr(sK + lds_off<HD>(key0 + 4, d)));
-          aq[dt] = mfma32(a, b, aq[dt]);
-        }
-      }
-      // element i of block dt: row 32*wave + (i/4)*8 + 4*(lane/32) + i%4, d = 32dt + lane%32
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = wave * 32 + (i >> 2) * 8 + 4 * (lane >> 5) + (i & 3);
-        const int64_t base = sAcc[m];
-        if (base >= 0) {
-#pragma unroll
-          for (int dt = 0; dt < DH; ++dt)
-            atomicAdd(dq_acc + base + (dpass * DH + dt) * 32 + (lane & 31), mt.scale * aq[dt][i]);
-        }
-      }
-    }
+  for (int qi = kt.qt_begin; qi < kt.qt_end; qi += 2) {
+    wait_async_loads();
+    __syncthreads();  // tile qi is in buffer 0; every wave is done with buffer 1
+    if (qi + 1 < kt.qt_end) prefetch(qi + 1, sQ1, sO1, sL1, sD1, sE1);
+    dkdv_tile<HD>(st, sQ0, sO0, sL0, sD0, sE0, sl2);
+    if (qi + 1 >= kt.qt_end) break;
+    wait_async_loads();
+    __syncthreads();  // tile qi+1 is in buffer 1; every wave is done with buffer 0
+    if (qi + 2 < kt.qt_end) prefetch(qi + 2, sQ0, sO0, sL0, sD0, sE0);
+    dkdv_tile<HD>(st, sQ1, sO1, sL1, sD1, sE1, sl2);
   }
 
   // dK, dV of the wave's keys: element i of block dt is key 32*wave +
@@ -257,22 +419,48 @@ __global__ __launch_bounds__(256) void main_bwd_bf16_kernel(Meta mt, const bf16 
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int64_t dst = ((int64_t)key * hkv + g) * HD + dt * 32 + (lane & 31);
-        dk[dst] = (bf16)(mt.scale * adk[dt][i]);
-        dv[dst] = (bf16)adv[dt][i];
+        dk[dst] = (bf16)(mt.scale * st.adk[dt][i]);
+        dv[dst] = (bf16)st.adv[dt][i];
       }
     }
   }
 }
 
-hipError_t launch_main_bwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *v,
-                                const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
-                                const float *delta, float *dq_acc, bf16 *dk, bf16 *dv, hipStream_t st) {
+hipError_t launch_bwd_gather_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *o, const bf16 *ob,
+                                  const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
+                                  float *delta, bf16 *qt, bf16 *dot, float *lt, float *dtt, int *et, hipStream_t st) {
+  if (mt.n_qtiles == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((int64_t)mt.n_qtiles * mt.hkv);
+  if (mt.d == 128)
+    bwd_gather_bf16_kernel<128><<<grid, 256, 0, st>>>(mt, q, qb, o, ob, d_o, d_ob, lse, lseb, delta, qt, dot, lt,
+                                                      dtt, et);
+  else
+    bwd_gather_bf16_kernel<64><<<grid, 256, 0, st>>>(mt, q, qb, o, ob, d_o, d_ob, lse, lseb, delta, qt, dot, lt,
+                                                     dtt, et);
+  return hipGetLastError();
+}
+
+hipError_t launch_main_bwd_dq_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *v,
+                                   const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
+                                   const float *delta, float *dq_acc, hipStream_t st) {
+  if (mt.n_qtiles == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((int64_t)mt.n_qtiles * mt.hkv);
+  if (mt.d == 128)
+    main_bwd_dq_bf16_kernel<128><<<grid, 256, 0, st>>>(mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, dq_acc);
+  else
+    main_bwd_dq_bf16_kernel<64><<<grid, 256, 0, st>>>(mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, dq_acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_main_bwd_dkdv_bf16(const Meta &mt, const bf16 *k, const bf16 *v, const bf16 *qt, const bf16 *dot,
+                                     const float *lt, const float *dtt, const int *et, bf16 *dk, bf16 *dv,
+                                     hipStream_t st) {
   if (mt.n_ktiles == 0) return hipSuccess;
   const unsigned grid = (unsigned)((int64_t)mt.n_ktiles * mt.hkv);
   if (mt.d == 128)
-    main_bwd_bf16_kernel<128><<<grid, 256, 0, st>>>(mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, dq_acc, dk, dv);
+    main_bwd_dkdv_bf16_kernel<128><<<grid, 256, 0, st>>>(mt, k, v, qt, dot, lt, dtt, et, dk, dv);
   else
-    main_bwd_bf16_kernel<64><<<grid, 256, 0, st>>>(mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, dq_acc, dk, dv);
+    main_bwd_dkdv_bf16_kernel<64><<<grid, 256, 0, st>>>(mt, k, v, qt, dot, lt, dtt, et, dk, dv);
   return hipGetLastError();
 }
 

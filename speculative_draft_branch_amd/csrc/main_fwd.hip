@@ -15,15 +15,104 @@
 // tile. The grid is longest-first; blockIdx % Hkv selects the kv head, so with
 // 8 kv heads each XCD streams one kv head's keys.
 //
+// K/V tiles are double-buffered: global_load_lds writes the next tile straight
+// into LDS while the current one is consumed; one barrier per tile.
+//
 // Per wave (32 query rows): S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so each
 // lane owns one query row (lane % 32) and row max/sum need a single exchange
 // between the two wave halves; P^T feeds O^T += V^T P^T straight from
-// registers, with V read from LDS by the transposing ds_read_b64_tr_b16.
+// registers, with V read from LDS by the transposing ds_read_b64_tr_b16. The
+// running max is only raised (and O, l rescaled) when a row's max grows by more
+// than 2^8, which keeps P <= 256 and skips almost every rescale.
 #include <climits>
 
 #include "launch.hpp"
 
 namespace ba {
+
+namespace {
+
+constexpr float kRescaleSlack = 8.0f;  // log2 units
+
+template <int HD>
+struct FwdState {
+  static constexpr int KS = HD / 16;
+  static constexpr int DT = HD / 32;
+  bf16x8 qf[KS];
+  f32x16 acc[DT];
+  float m_run, l_run;
+  int end, wmin, wmax;
+  int grp, in_j, in_q, lane;
+};
+
+// One 64-key tile [k0, k0 + 64) of the wave's 32 rows against LDS tiles sK, sV.
+template <int HD>
+__device__ __forceinline__ void fwd_tile(FwdState<HD> &st, const bf16 *sK, const bf16 *sV, int k0, float sl2) {
+  constexpr int KS = FwdState<HD>::KS, DT = FwdState<HD>::DT;
+  const int lane = st.lane;
+  // S^T[key][row] for two 32-key blocks.
+  f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int r = kb * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch = 2 * ks + (lane >> 5);
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sK + r * HD + ((ch ^ swz<HD>(r)) << 3));
+      s[kb] = mfma32(a, st.qf[ks], s[kb]);
+    }
+  }
+  if (k0 + 63 > st.wmin) {  // some key of this tile lies past some row's prefix end
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+        if (key > st.end) s[kb][i] = -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+  const float mt = half_max(mx) * sl2;
+  if (__any(mt > st.m_run + kRescaleSlack)) {
+    const float m_new = fmaxf(st.m_run, mt);
+    const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(st.m_run - m_new);
+    st.l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
+    st.m_run = m_new;
+  }
+  const float m_use = (st.m_run == -INFINITY) ? 0.0f : st.m_run;
+  float rs = 0.0f;
+  bf16x8 pb[4];  // P^T operands of the four 16-key k-steps
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(fmaf(s[kb][i], sl2, -m_use));
+      rs += p;
+      pb[kb * 2 + (i >> 3)][i & 7] = (bf16)p;
+    }
+  st.l_run += rs;
+  // O^T += V^T P^T. k-step kk covers tile keys 16kk..16kk+15; operand slot
+  // 8*half + 4c + j <-> key 16kk + 8c + 4*half + j on both operands.
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int key0 = kk * 16 + 4 * (st.grp >> 1) + st.in_j;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = dt * 32 + (st.grp & 1) * 16 + 4 * st.in_q;
+      const i16x4 t0 = lds_read_tr(sV + lds_off<HD>(key0, d));
+      const i16x4 t1 = lds_read_tr(sV + lds_off<HD>(key0 + 8, d));
+      st.acc[dt] = mfma32(join(t0, t1), pb[kk], st.acc[dt]);
+    }
+  }
+}
+
+}  // namespace
 
 template <int HD>
 __global__ __launch_bounds__(256) void main_fwd_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
@@ -32,135 +121,82 @@ __global__ __launch_bounds__(256) void main_fwd_bf16_kernel(Meta mt, const bf16 
                                                             const bf16 *__restrict__ v, bf16 *__restrict__ o,
                                                             float *__restrict__ lse, float *__restrict__ o_pre,
                                                             float *__restrict__ lse_pre) {
-  constexpr int BN = 64;        // keys per K/V tile
-  constexpr int NCH = HD / 8;   // 16-byte chunks per key row
-  constexpr int KS = HD / 16;   // MFMA k-steps over head_dim
-  constexpr int DT = HD / 32;   // 32-wide output blocks over head_dim
-  __shared__ __attribute__((aligned(16))) bf16 sK[BN * HD];
-  __shared__ __attribute__((aligned(16))) bf16 sV[BN * HD];
+  constexpr int BN = 64;  // keys per K/V tile
+  constexpr int KS = HD / 16, DT = HD / 32;
+  __shared__ __attribute__((aligned(16))) bf16 sK0[BN * HD];
+  __shared__ __attribute__((aligned(16))) bf16 sV0[BN * HD];
+  __shared__ __attribute__((aligned(16))) bf16 sK1[BN * HD];
+  __shared__ __attribute__((aligned(16))) bf16 sV1[BN * HD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hkv = mt.hkv, G = mt.G;
   const int g = blockIdx.x % hkv;
-  const QTile tile = mt.qtiles[mt.fwd_order[blockIdx.x / hkv]];
+  const QTile tile = load_qtile(mt.qtiles + uni(mt.fwd_order[blockIdx.x / hkv]));
+  const int kv_lo = tile.kv_lo, kv_end = tile.end_max;
+  const int ntiles = (kv_end - kv_lo + BN) / BN;
+
+  // Start fetching the first K/V tile before anything else.
+  stage_rows_async<HD, BN, 256>(sK0, k, hkv, g, kv_lo, kv_end, tid);
+  stage_rows_async<HD, BN, 256>(sV0, v, hkv, g, kv_lo, kv_end, tid);
 
   // This lane's query row: MFMA row 32*wave + lane%32 = base row * G + head.
+  FwdState<HD> st;
   const int mrow = wave * 32 + (lane & 31);
   const int bi = mrow / G, hj = mrow - bi * G;
-  int row = -1, end = -1;
+  int row = -1;
+  st.end = -1;
   if (bi < tile.nrows) {
     row = mt.tile_row_id[tile.row_begin + bi];
-    end = mt.tile_row_end[tile.row_begin + bi];
+    st.end = mt.tile_row_end[tile.row_begin + bi];
   }
   const int h = mt.group_heads[g * G + hj];
   const bool is_main = row >= 0 && row < mt.Nq;
   const int64_t roff = row < 0 ? 0
                        : is_main ? ((int64_t)row * mt.hq + h) * HD
                                  : ((int64_t)(row - mt.Nq) * mt.hq + h) * HD;
-
   // Q as the B operand: lane holds row lane%32, d = 16*ks + 8*(lane/32) + 0..7.
-  bf16x8 qf[KS];
   {
     const bf16 *qp = (is_main ? q : qb) + roff + 8 * (lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (row >= 0) qf[ks] = *reinterpret_cast<const bf16x8 *>(qp + 16 * ks);
-      else qf[ks] = bf16x8{};
+      if (row >= 0) st.qf[ks] = *reinterpret_cast<const bf16x8 *>(qp + 16 * ks);
+      else st.qf[ks] = bf16x8{};
     }
   }
-  const int wmin = wave_min(row >= 0 ? end : INT_MAX);
-  const int wmax = wave_max(end);
-
+  st.wmin = wave_min(row >= 0 ? st.end : INT_MAX);
+  st.wmax = wave_max(st.end);
+  st.m_run = -INFINITY;
+  st.l_run = 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) st.acc[dt] = f32x16{};
+  st.lane = lane;
+  st.grp = lane >> 4;
+  st.in_j = (lane & 15) >> 2;
+  st.in_q = lane & 3;
   const float sl2 = mt.scale * kLog2e;
-  float m_run = -INFINITY, l_run = 0.0f;
-  f32x16 acc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
-  // transposed-read coordinates of this lane (as an input lane of its 16-lane group)
-  const int grp = lane >> 4, in_j = (lane & 15) >> 2, in_q = lane & 3;
-
-  const int kv_end = tile.end_max;
-  for (int k0 = tile.kv_lo; k0 <= kv_end; k0 += BN) {
-#pragma unroll
-    for (int it = 0; it < BN * NCH / 256; ++it) {
-      const int c = tid + it * 256;
-      const int r = c / NCH, ch = c % NCH;
-      const int key = k0 + r;
-      uint4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-      if (key <= kv_end) {
-        const int64_t src = ((int64_t)key * hkv + g) * HD + ch * 8;
-        kx = *reinterpret_cast<const uint4 *>(k + src);
-        vx = *reinterpret_cast<const uint4 *>(v + src);
-      }
-      const int dst = r * HD + ((ch ^ swz<HD>(r)) << 3);
-      *reinterpret_cast<uint4 *>(sK + dst) = kx;
-      *reinterpret_cast<uint4 *>(sV + dst) = vx;
+  // Tiles alternate between the two buffers; the loop is unrolled by two so
+  // each buffer is a distinct LDS object.
+  for (int j = 0; j < ntiles; j += 2) {
+    const int k0 = kv_lo + j * BN;
+    wait_async_loads();
+    __syncthreads();  // tile j is in buffer 0; every wave is done with buffer 1
+    if (j + 1 < ntiles) {
+      stage_rows_async<HD, BN, 256>(sK1, k, hkv, g, k0 + BN, kv_end, tid);
+      stage_rows_async<HD, BN, 256>(sV1, v, hkv, g, k0 + BN, kv_end, tid);
     }
-    __syncthreads();
-    if (k0 <= wmax) {
-      // S^T[key][row] for two 32-key blocks.
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int r = kb * 32 + (lane & 31);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int ch = 2 * ks + (lane >> 5);
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sK + r * HD + ((ch ^ swz<HD>(r)) << 3));
-          s[kb] = mfma32(a, qf[ks], s[kb]);
-        }
-      }
-      if (k0 + BN - 1 > wmin) {  // some key of this tile lies past some row's prefix end
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-            if (key > end) s[kb][i] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = half_max(mx);
-      const float m_new = fmaxf(m_run, mx * sl2);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float rs = 0.0f;
-      bf16x8 pb[4];  // P^T operands of the four 16-key k-steps
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(s[kb][i], sl2, -m_use));
-          rs += p;
-          pb[kb * 2 + (i >> 3)][i & 7] = (bf16)p;
-        }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-      // O^T += V^T P^T. k-step kk covers tile keys 16kk..16kk+15; operand slot
-      // 8*half + 4c + j <-> key 16kk + 8c + 4*half + j on both operands.
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int key0 = kk * 16 + 4 * (grp >> 1) + in_j;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int d = dt * 32 + (grp & 1) * 16 + 4 * in_q;
-          const i16x4 t0 = lds_read_tr(sV + lds_off<HD>(key0, d));
-          const i16x4 t1 = lds_read_tr(sV + lds_off<HD>(key0 + 8, d));
-          acc[dt] = mfma32(join(t0, t1), pb[kk], acc[dt]);
-        }
-      }
+    if (k0 <= st.wmax) fwd_tile<HD>(st, sK0, sV0, k0, sl2);
+    if (j + 1 >= ntiles) break;
+    wait_async_loads();
+    __syncthreads();  // tile j+1 is in buffer 1; every wave is done with buffer 0
+    if (j + 2 < ntiles) {
+      stage_rows_async<HD, BN, 256>(sK0, k, hkv, g, k0 + 2 * BN, kv_end, tid);
+      stage_rows_async<HD, BN, 256>(sV0, v, hkv, g, k0 + 2 * BN, kv_end, tid);
     }
-    __syncthreads();
+    if (k0 + BN <= st.wmax) fwd_tile<HD>(st, sK1, sV1, k0 + BN, sl2);
   }
 
-  const float l_tot = half_sum(l_run);
+  const float l_tot = half_sum(st.l_run);
   if (row >= 0) {
     const float inv = 1.0f / l_tot;
 #pragma unroll
@@ -168,8 +204,8 @@ __global__ __launch_bounds__(256) void main_fwd_bf16_kernel(Meta mt, const bf16 
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = dt * 32 + q4 * 8 + (lane >> 5) * 4;
-        const f32x4 val = {acc[dt][q4 * 4 + 0] * inv, acc[dt][q4 * 4 + 1] * inv, acc[dt][q4 * 4 + 2] * inv,
-                           acc[dt][q4 * 4 + 3] * inv};
+        const f32x4 val = {st.acc[dt][q4 * 4 + 0] * inv, st.acc[dt][q4 * 4 + 1] * inv,
+                           st.acc[dt][q4 * 4 + 2] * inv, st.acc[dt][q4 * 4 + 3] * inv};
         if (is_main) {
           const bf16x4 b = {(bf16)val[0], (bf16)val[1], (bf16)val[2], (bf16)val[3]};
           *reinterpret_cast<bf16x4 *>(o + roff + d) = b;
@@ -178,7 +214,7 @@ __global__ __launch_bounds__(256) void main_fwd_bf16_kernel(Meta mt, const bf16 
         }
       }
     if (lane < 32) {
-      const float lv = (m_run + __log2f(l_tot)) * kLn2;
+      const float lv = (st.m_run + __log2f(l_tot)) * kLn2;
       if (is_main) lse[(int64_t)h * mt.Nq + row] = lv;
       else lse_pre[(int64_t)h * mt.Rb + (row - mt.Nq)] = lv;
     }

@@ -273,7 +273,21 @@ void build(ba_plan *pl) {
   pl->off_delta = base;
   size_t d_bytes = align_up((size_t)R * pl->hq * f32, 256);
   pl->off_dq_acc = pl->off_delta + d_bytes;
-  pl->ws_bwd = pl->off_dq_acc + align_up((size_t)R * pl->hq * pl->d * f32, 256);
+  size_t cur_b = pl->off_dq_acc + align_up((size_t)R * pl->hq * pl->d * f32, 256);
+  const size_t tiles_g = (size_t)pl->n_qtiles * pl->hkv;
+  if (pl->dtype == BA_BF16) {
+    const size_t row_bytes = align_up(tiles_g * kTileRows * pl->d * 2, 256);
+    const size_t scal_bytes = align_up(tiles_g * kTileRows * f32, 256);
+    pl->off_qt = cur_b;
+    pl->off_dot = pl->off_qt + row_bytes;
+    pl->off_lt = pl->off_dot + row_bytes;
+    pl->off_dt = pl->off_lt + scal_bytes;
+    pl->off_et = pl->off_dt + scal_bytes;
+    cur_b = pl->off_et + align_up((size_t)pl->n_qtiles * kTileMetaWords * 4, 256);
+  } else {
+    pl->off_qt = pl->off_dot = pl->off_lt = pl->off_dt = pl->off_et = cur_b;
+  }
+  pl->ws_bwd = cur_b;
 }
 
 }  // namespace

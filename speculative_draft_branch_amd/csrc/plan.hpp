@@ -15,6 +15,10 @@ namespace ba {
 constexpr int kTileRows = 128;
 // Keys per backward key tile.
 constexpr int kBwdKeys = 128;
+// Per-query-tile block of row ends the backward gather writes: 128 prefix ends,
+// then the tile's smallest end, largest end and valid MFMA rows (padded to 3 x 64
+// words for whole-wave LDS copies).
+constexpr int kTileMetaWords = 192;
 // Longest branch the branch-local kernels handle.
 constexpr int kMaxBranch = 32;
 
@@ -75,6 +79,9 @@ struct ba_plan {
   // workspace regions (byte offsets)
   size_t off_o_pre, off_lse_pre, off_o_loc, off_lse_loc;  // forward
   size_t off_delta, off_dq_acc;                           // backward
+  // backward, query-tile order per kv head: Q and dO rows [n_qtiles][Hkv][128][d],
+  // LSE*log2(e) and D [n_qtiles][Hkv][128], row-end blocks [n_qtiles][kTileMetaWords]
+  size_t off_qt, off_dot, off_lt, off_dt, off_et;
 };
 
 namespace ba {
