@@ -44,39 +44,39 @@ template <int HD>
 __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const bf16 *sV, int k0, float sl2) {
   constexpr int KS = DqState<HD>::KS, DT = DqState<HD>::DT;
   const int lane = st.lane;
-  f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+  const bool need_mask = k0 + 63 > st.wmin;
+  // One 32-key block at a time: S^T, dP^T, dS^T, then its two dQ k-steps.
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
+    f32x16 s = f32x16{}, dp = f32x16{};
     const int r = kb * 32 + (lane & 31);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int off = r * HD + (((2 * ks + (lane >> 5)) ^ swz<HD>(r)) << 3);
-      s[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(sK + off), st.qf[ks], s[kb]);
-      dp[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(sV + off), st.of[ks], dp[kb]);
+      s = mfma32(*reinterpret_cast<const bf16x8 *>(sK + off), st.qf[ks], s);
+      dp = mfma32(*reinterpret_cast<const bf16x8 *>(sV + off), st.of[ks], dp);
     }
-  }
-  const bool need_mask = k0 + 63 > st.wmin;
-  bf16x8 db[4];  // dS^T operands of the four 16-key k-steps
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    bf16x8 db[2];  // dS^T operands of the block's two 16-key k-steps
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float p = fast_exp2(fmaf(s[kb][i], sl2, -st.l2));
+      float p = fast_exp2(fmaf(s[i], sl2, -st.l2));
       if (need_mask) {
         const int key = k0 + kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
         if (key > st.end) p = 0.0f;
       }
-      db[kb * 2 + (i >> 3)][i & 7] = (bf16)(p * (dp[kb][i] - st.dd));
+      db[i >> 3][i & 7] = (bf16)(p * (dp[i] - st.dd));
     }
-  // dQ^T += K^T dS^T; slot 8*half + 4c + j <-> key 16kk + 8c + 4*half + j.
+    // dQ^T += K^T dS^T; slot 8*half + 4c + j <-> key 16kk + 8c + 4*half + j.
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int key0 = kk * 16 + 4 * (st.grp >> 1) + st.in_j;
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int kk = kb * 2 + h2;
+      const int key0 = kk * 16 + 4 * (st.grp >> 1) + st.in_j;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = dt * 32 + (st.grp & 1) * 16 + 4 * st.in_q;
-      const bf16x8 a = join(lds_read_tr(sK + lds_off<HD>(key0, d)), lds_read_tr(sK + lds_off<HD>(key0 + 8, d)));
-      st.acc[dt] = mfma32(a, db[kk], st.acc[dt]);
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = dt * 32 + (st.grp & 1) * 16 + 4 * st.in_q;
+        const bf16x8 a = join(lds_read_tr(sK + lds_off<HD>(key0, d)), lds_read_tr(sK + lds_off<HD>(key0 + 8, d)));
+        st.acc[dt] = mfma32(a, db[h2], st.acc[dt]);
+      }
     }
   }
 }
@@ -84,7 +84,7 @@ __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const b
 }  // namespace
 
 template <int HD>
-__global__ __launch_bounds__(256) void main_bwd_dq_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
+__global__ __launch_bounds__(256, 2) void main_bwd_dq_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
                                                                const bf16 *__restrict__ qb,
                                                                const bf16 *__restrict__ k,
                                                                const bf16 *__restrict__ v,

@@ -115,7 +115,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<HD> &st, const bf16 *sK, const
 }  // namespace
 
 template <int HD>
-__global__ __launch_bounds__(256) void main_fwd_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
+__global__ __launch_bounds__(256, 2) void main_fwd_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
                                                             const bf16 *__restrict__ qb,
                                                             const bf16 *__restrict__ k,
                                                             const bf16 *__restrict__ v, bf16 *__restrict__ o,
