@@ -289,10 +289,10 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<HD> &st, const bf16 *sQ, con
   const int end_min = uni(sEnd[BM]), end_max = uni(sEnd[BM + 1]), valid_rows = uni(sEnd[BM + 2]);
   if (end_max < st.wkey_lo || st.wkey_lo >= st.key_hi) return;  // no row of this tile sees the wave's keys
   const bool need_mask = end_min < st.wkey_lo + 31 || st.wkey_lo + 31 >= st.key_hi || valid_rows < BM;
-#pragma unroll
-  for (int rb = 0; rb < BM / 32; ++rb) {
-    // S and dP for rows 32rb..32rb+31 x the wave's 32 keys.
-    f32x16 s = f32x16{}, dp = f32x16{};
+  // S and dP of row block rb (rows 32rb..32rb+31) x the wave's 32 keys.
+  auto scores = [&](int rb, f32x16 &s, f32x16 &dp) {
+    s = f32x16{};
+    dp = f32x16{};
     const int ar = rb * 32 + (lane & 31);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -300,6 +300,15 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<HD> &st, const bf16 *sQ, con
       s = mfma32(*reinterpret_cast<const bf16x8 *>(sQ + off), st.kf[ks], s);
       dp = mfma32(*reinterpret_cast<const bf16x8 *>(sdO + off), st.vf[ks], dp);
     }
+  };
+  // Software-pipelined over the row blocks: the S/dP products of block rb+1
+  // are issued before block rb's exponentials, so MFMA and VALU work overlap.
+  f32x16 s_nx, dp_nx;
+  scores(0, s_nx, dp_nx);
+#pragma unroll
+  for (int rb = 0; rb < BM / 32; ++rb) {
+    const f32x16 s = s_nx, dp = dp_nx;
+    if (rb + 1 < BM / 32) scores(rb + 1, s_nx, dp_nx);
     // element i: row rb*32 + (i/4)*8 + 4*(lane/32) + i%4, key my_key
     bf16x8 pa[2], dsa[2];
 #pragma unroll

@@ -110,3 +110,37 @@ def test_workspace_sizes_cover_partials():
     assert p.workspace_bytes(0) >= 2 * w.Rb * w.num_q_heads * w.head_dim * f32
     assert p.workspace_bytes(1) >= (w.Nq + w.Rb) * w.num_q_heads * (w.head_dim + 1) * f32
     assert 0 < p.workspace_bytes(2) <= p.workspace_bytes(0)
+
+
+def test_timing_api_without_launches():
+    """The opt-in timing calls work on the host alone: names for every kernel id,
+    zero totals when nothing was recorded, and argument checks."""
+    sda.timing_reset()
+    sda.timing_enable(True)
+    sda.timing_enable(False)
+    rec = sda.timing_read()
+    assert {"main_fwd", "main_bwd_dq", "main_bwd_dkdv", "lse_merge", "branch_local_fwd"} <= set(rec)
+    assert all(v == (0.0, 0) for v in rec.values())
+    lib = sda.lib
+    assert lib.ba_timing_kernel_name(-1) is None
+    assert lib.ba_timing_kernel_name(lib.ba_timing_kernels()) is None
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert lib.ba_timing_read(lib.ba_timing_kernels(), ctypes.byref(ms), ctypes.byref(n)) == BA_EINVAL
+
+
+def test_entry_points_reject_bad_arguments_without_touching_the_gpu():
+    """Structural argument errors are reported before anything is enqueued."""
+    w = W.get("tiny_f32")
+    p = Plan.from_workload(w)
+    lib = sda.lib
+    # NULL plan, NULL tensors, short workspace, misaligned pointers
+    assert lib.branch_attn_fwd(None, *([None] * 10), None, 0, None) == BA_EINVAL
+    fake = 1 << 40  # never dereferenced: checks fail first
+    args = [fake] * 6 + [fake] * 4
+    assert lib.branch_attn_fwd(p.handle, *args, None, 0, None) == sda.BA_EWORKSPACE
+    assert lib.branch_attn_fwd(p.handle, *args, fake, 16, None) == sda.BA_EWORKSPACE
+    bad = list(args)
+    bad[0] = fake + 2
+    assert lib.branch_attn_fwd(p.handle, *bad, fake, p.workspace_bytes(0), None) == BA_EINVAL
+    assert lib.lse_merge(10, 2, 6, fake, fake, fake, fake, fake, 0, fake, None) == BA_EINVAL  # d/4 must divide 64
+    assert lib.lse_merge(10, 2, 64, fake, fake, fake, fake, fake, 7, fake, None) == BA_EINVAL  # bad dtype
