@@ -134,6 +134,9 @@ def main():
     ap.add_argument("--workload", default="ctx256k_rank3")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="before the warmup, copy a buffer of this many MiB once (a plain copy kernel of known "
+                         "size, for scaling hardware byte counters); not part of the timed region")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -170,6 +173,16 @@ def main():
         sda.branch_attn_fwd(plan, g["q"], g["k"], g["v"], g["qb"], g["kb"], g["vb"], o, lse, ob, lseb, ws_f)
         sda.branch_attn_bwd(plan, g["q"], g["k"], g["v"], g["qb"], g["kb"], g["vb"], o, lse, ob, lseb,
                             g["do"], g["dob"], *gr, ws_b)
+
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.calibration_copy_mib} MiB done")
+        del src, dst
 
     for i in range(args.warmup):
         step()

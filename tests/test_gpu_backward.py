@@ -14,7 +14,7 @@ import workloads as W
 from workloads.configs import custom, TTT, BLOCK
 from workloads.inputs import make_inputs, to_f32
 
-from gpu_util import say, dev, host, check_out, f64_all, f32_views, sample_rows, rel_l2
+from gpu_util import say, dev, host, check_out, f64_all, f32_views, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -112,6 +112,7 @@ def test_backward_full_size(name):
     tv = f32_views(t)
     # dQ of sampled rows, exact per row
     rows = sample_rows(w, n_random=8, seed=9)
+    say(f"  dq of {len(rows)} sampled rows")
     ref = oracle.backward_rows(p, tv, rows)
     Nq = w.Nq
     got_rows = np.stack([host(got["dq"][r]) if r < Nq else host(got["dqb"][r - Nq]) for r in rows])
@@ -128,19 +129,19 @@ def test_backward_full_size(name):
     acc = {"dk": np.zeros((w.N, w.num_kv_heads, w.head_dim)), "dv": np.zeros((w.N, w.num_kv_heads, w.head_dim)),
            "dkb": np.zeros((w.Rb, w.num_kv_heads, w.head_dim)), "dvb": np.zeros((w.Rb, w.num_kv_heads, w.head_dim))}
     say(f"  exact dK/dV of keys {u0}..{hi - 1}: {len(see)} rows")
-    oracle.backward_rows(p, tv, see, acc)
+    for c0 in range(0, len(see), 16):
+        oracle.backward_rows(p, tv, see[c0:c0 + 16], acc)
+        say(f"    oracle rows {c0 + len(see[c0:c0 + 16])}/{len(see)}")
     check_out("dk(last keys)", host(got["dk"][u0:hi]), acc["dk"][u0:hi], "bf16", "grad")
     check_out("dv(last keys)", host(got["dv"][u0:hi]), acc["dv"][u0:hi], "bf16", "grad")
 
 
-def test_backward_is_run_to_run_stable():
-    """dK/dV are written once per key (bitwise reproducible); dQ is accumulated
-    with atomics, so it may differ in the last bits only."""
+def test_backward_is_deterministic():
+    """Every gradient is written once per element by one workgroup, with no
+    atomics, so two runs agree bitwise."""
     w = W.get("ctx256k_rank3_chunk64")
     t = make_inputs(w, grads=True)
     _, _, _, a = _run(w, t)
     _, _, _, b = _run(w, t)
-    for k_ in ("dk", "dv", "dkb", "dvb"):
+    for k_ in GRADS:
         assert torch.equal(a[k_], b[k_]), k_
-    for k_ in ("dq", "dqb"):
-        assert rel_l2(host(a[k_]), host(b[k_])) <= 1e-3
