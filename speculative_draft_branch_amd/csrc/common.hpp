@@ -135,30 +135,66 @@ __device__ __forceinline__ void stage_rows(bf16 *lds, const bf16 *__restrict__ s
   }
 }
 
-// Asynchronous form of stage_rows: global_load_lds (16 bytes per lane, gfx950)
-// writes each wave's 1 KB block of the swizzled tile straight into LDS, so lane
-// l of block b fetches the logical chunk that the swizzle places at LDS offset
-// b*1KB + 16*l. Rows past `last` are clamped to `last` (callers mask those
-// keys). Completion is tracked by vmcnt: wait_async_loads() then a barrier
-// before the tile is read.
+// Asynchronous staging of a [ROWS x HD] bf16 tile into LDS with global_load_lds
+// (16 bytes per lane, gfx950): each wave's 1 KB block of the swizzled tile is
+// written straight into LDS, lane l of block b fetching the logical chunk that
+// the swizzle places at LDS offset b*1KB + 16*l. Completion is tracked by
+// vmcnt: wait_async_loads() then a barrier before the tile is read.
+//
+// The per-lane part of each address (row within the tile, chunk) is fixed for
+// the kernel's life, so it is computed once; a tile only moves the uniform base.
+template <int HD, int ROWS, int NT>
+struct AsyncTile {
+  static constexpr int NCH = HD / 8;         // 16-byte chunks per row
+  static constexpr int RPB = 64 / NCH;       // rows per 1 KB wave block
+  static constexpr int BLOCKS = ROWS / RPB;  // 1 KB blocks in the tile
+  static_assert(BLOCKS % (NT / 64) == 0, "tile must split evenly over the waves");
+  static constexpr int PER_WAVE = BLOCKS / (NT / 64);
+  int row[PER_WAVE];        // tile row of this lane's chunk in each of its wave's blocks
+  uint32_t off[PER_WAVE];   // byte offset of that chunk from the tile's first row
+  int lds_block;            // first 1 KB block of this wave (wave-uniform)
+  int row_stride;           // elements between consecutive rows in global memory
+
+  __device__ __forceinline__ void init(int row_stride_elems, int tid) {
+    const int lane = tid & 63;
+    row_stride = row_stride_elems;
+    lds_block = uni(tid >> 6) * PER_WAVE;
+#pragma unroll
+    for (int it = 0; it < PER_WAVE; ++it) {
+      const int r = (lds_block + it) * RPB + lane / NCH;
+      row[it] = r;
+      off[it] = (uint32_t)(r * row_stride_elems + (((lane % NCH) ^ swz<HD>(r)) << 3)) * 2u;
+    }
+  }
+  // Tile rows [k0, k0 + ROWS) from `base` (pointer to row 0 of the tensor,
+  // already offset to the kv head); rows past `last` are clamped to `last`.
+  __device__ __forceinline__ void load(bf16 *lds, const bf16 *__restrict__ base, int k0, int last) const {
+    const char *tb = reinterpret_cast<const char *>(base + (int64_t)k0 * row_stride);
+    if (k0 + ROWS - 1 <= last) {
+#pragma unroll
+      for (int it = 0; it < PER_WAVE; ++it)
+        __builtin_amdgcn_global_load_lds(tb + off[it],
+                                         (__attribute__((address_space(3))) void *)(lds + (lds_block + it) * 512),
+                                         16, 0, 0);
+    } else {
+#pragma unroll
+      for (int it = 0; it < PER_WAVE; ++it) {
+        // rows past the end read row `last` instead (callers mask those keys)
+        const uint32_t back = (uint32_t)max(k0 + row[it] - last, 0) * (uint32_t)row_stride * 2u;
+        __builtin_amdgcn_global_load_lds(tb + (off[it] - back),
+                                         (__attribute__((address_space(3))) void *)(lds + (lds_block + it) * 512),
+                                         16, 0, 0);
+      }
+    }
+  }
+};
+
 template <int HD, int ROWS, int NT>
 __device__ __forceinline__ void stage_rows_async(bf16 *lds, const bf16 *__restrict__ src, int hkv, int g, int k0,
                                                  int last, int tid) {
-  constexpr int NCH = HD / 8;          // 16-byte chunks per row
-  constexpr int RPB = 64 / NCH;        // rows per 1 KB wave block
-  constexpr int BLOCKS = ROWS / RPB;   // 1 KB blocks in the tile
-  static_assert(BLOCKS % (NT / 64) == 0, "tile must split evenly over the waves");
-  constexpr int PER_WAVE = BLOCKS / (NT / 64);
-  const int lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-  for (int it = 0; it < PER_WAVE; ++it) {
-    const int b = wave * PER_WAVE + it;
-    const int r = b * RPB + lane / NCH;
-    const int ch = (lane % NCH) ^ swz<HD>(r);
-    const int key = min(k0 + r, last);
-    const bf16 *gp = src + ((int64_t)key * hkv + g) * HD + ch * 8;
-    __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void *)(lds + b * 512), 16, 0, 0);
-  }
+  AsyncTile<HD, ROWS, NT> t;
+  t.init(hkv * HD, tid);
+  t.load(lds, src + (int64_t)g * HD, k0, last);
 }
 
 // Asynchronous copy of 64*n consecutive 32-bit words into LDS by one wave

@@ -108,8 +108,11 @@ __global__ __launch_bounds__(256, 2) void main_bwd_dq_bf16_kernel(Meta mt, const
   const int64_t R = mt.Nq + mt.Rb;
   const int kv_lo = tile.kv_lo, kv_end = tile.end_max;
   const int ntiles = (kv_end - kv_lo + BN) / BN;
-  stage_rows_async<HD, BN, 256>(sK0, k, hkv, g, kv_lo, kv_end, tid);
-  stage_rows_async<HD, BN, 256>(sV0, v, hkv, g, kv_lo, kv_end, tid);
+  AsyncTile<HD, BN, 256> kvt;
+  kvt.init(hkv * HD, tid);
+  const bf16 *kg = k + (int64_t)g * HD, *vg = v + (int64_t)g * HD;
+  kvt.load(sK0, kg, kv_lo, kv_end);
+  kvt.load(sV0, vg, kv_lo, kv_end);
 
   DqState<HD> st;
   const int mrow = wave * 32 + (lane & 31);
@@ -160,16 +163,16 @@ __global__ __launch_bounds__(256, 2) void main_bwd_dq_bf16_kernel(Meta mt, const
     wait_async_loads();
     __syncthreads();  // tile j is in buffer 0; every wave is done with buffer 1
     if (j + 1 < ntiles) {
-      stage_rows_async<HD, BN, 256>(sK1, k, hkv, g, k0 + BN, kv_end, tid);
-      stage_rows_async<HD, BN, 256>(sV1, v, hkv, g, k0 + BN, kv_end, tid);
+      kvt.load(sK1, kg, k0 + BN, kv_end);
+      kvt.load(sV1, vg, k0 + BN, kv_end);
     }
     if (k0 <= wmax) dq_tile<HD>(st, sK0, sV0, k0, sl2);
     if (j + 1 >= ntiles) break;
     wait_async_loads();
     __syncthreads();  // tile j+1 is in buffer 1; every wave is done with buffer 0
     if (j + 2 < ntiles) {
-      stage_rows_async<HD, BN, 256>(sK0, k, hkv, g, k0 + 2 * BN, kv_end, tid);
-      stage_rows_async<HD, BN, 256>(sV0, v, hkv, g, k0 + 2 * BN, kv_end, tid);
+      kvt.load(sK0, kg, k0 + 2 * BN, kv_end);
+      kvt.load(sV0, vg, k0 + 2 * BN, kv_end);
     }
     if (k0 + BN <= wmax) dq_tile<HD>(st, sK1, sV1, k0 + BN, sl2);
   }
@@ -370,10 +373,12 @@ __global__ __launch_bounds__(256) void main_bwd_dkdv_bf16_kernel(Meta mt, const 
   const float sl2 = mt.scale * kLog2e;
 
   // Query tile qi, kv head g -> one LDS buffer (all asynchronous).
+  AsyncTile<HD, BM, 256> rowt;
+  rowt.init(HD, tid);
   auto prefetch = [&](int qi, bf16 *sQ, bf16 *sO, float *sL, float *sD, int *sE) {
     const int64_t tb = ((int64_t)qi * hkv + g) * BM;
-    stage_rows_async<HD, BM, 256>(sQ, qt_rows + tb * HD, 1, 0, 0, BM - 1, tid);
-    stage_rows_async<HD, BM, 256>(sO, do_rows + tb * HD, 1, 0, 0, BM - 1, tid);
+    rowt.load(sQ, qt_rows + tb * HD, 0, BM - 1);
+    rowt.load(sO, do_rows + tb * HD, 0, BM - 1);
     if (wave == 0) stage_words_async<BM / 64>(sL, lt + tb, lane);
     else if (wave == 1) stage_words_async<BM / 64>(sD, dtt + tb, lane);
     else if (wave == 2) stage_words_async<kTileMetaWords / 64>(sE, et + (int64_t)qi * kTileMetaWords, lane);

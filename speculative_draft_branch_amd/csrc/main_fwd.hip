@@ -135,9 +135,13 @@ __global__ __launch_bounds__(256, 2) void main_fwd_bf16_kernel(Meta mt, const bf
   const int kv_lo = tile.kv_lo, kv_end = tile.end_max;
   const int ntiles = (kv_end - kv_lo + BN) / BN;
 
-  // Start fetching the first K/V tile before anything else.
-  stage_rows_async<HD, BN, 256>(sK0, k, hkv, g, kv_lo, kv_end, tid);
-  stage_rows_async<HD, BN, 256>(sV0, v, hkv, g, kv_lo, kv_end, tid);
+  // Start fetching the first K/V tile before anything else. K and V share the
+  // layout, so one set of per-lane offsets serves both.
+  AsyncTile<HD, BN, 256> kvt;
+  kvt.init(hkv * HD, tid);
+  const bf16 *kg = k + (int64_t)g * HD, *vg = v + (int64_t)g * HD;
+  kvt.load(sK0, kg, kv_lo, kv_end);
+  kvt.load(sV0, vg, kv_lo, kv_end);
 
   // This lane's query row: MFMA row 32*wave + lane%32 = base row * G + head.
   FwdState<HD> st;
@@ -182,16 +186,16 @@ __global__ __launch_bounds__(256, 2) void main_fwd_bf16_kernel(Meta mt, const bf
     wait_async_loads();
     __syncthreads();  // tile j is in buffer 0; every wave is done with buffer 1
     if (j + 1 < ntiles) {
-      stage_rows_async<HD, BN, 256>(sK1, k, hkv, g, k0 + BN, kv_end, tid);
-      stage_rows_async<HD, BN, 256>(sV1, v, hkv, g, k0 + BN, kv_end, tid);
+      kvt.load(sK1, kg, k0 + BN, kv_end);
+      kvt.load(sV1, vg, k0 + BN, kv_end);
     }
     if (k0 <= st.wmax) fwd_tile<HD>(st, sK0, sV0, k0, sl2);
     if (j + 1 >= ntiles) break;
     wait_async_loads();
     __syncthreads();  // tile j+1 is in buffer 1; every wave is done with buffer 0
     if (j + 2 < ntiles) {
-      stage_rows_async<HD, BN, 256>(sK0, k, hkv, g, k0 + 2 * BN, kv_end, tid);
-      stage_rows_async<HD, BN, 256>(sV0, v, hkv, g, k0 + 2 * BN, kv_end, tid);
+      kvt.load(sK0, kg, k0 + 2 * BN, kv_end);
+      kvt.load(sV0, vg, k0 + 2 * BN, kv_end);
     }
     if (k0 + BN <= st.wmax) fwd_tile<HD>(st, sK1, sV1, k0 + BN, sl2);
   }
