@@ -15,11 +15,11 @@ namespace {
 // Opt-in per-kernel timing: HIP events recorded on the launch stream.
 enum KernelId {
   K_UPLOAD = 0, K_MAIN_FWD, K_BRANCH_LOCAL_FWD, K_LSE_MERGE, K_BWD_PREPROCESS, K_MAIN_BWD_DQ, K_MAIN_BWD_DKDV,
-  K_BRANCH_LOCAL_BWD, K_DQ_CONVERT, K_COUNT
+  K_BRANCH_LOCAL_BWD, K_DQ_CONVERT, K_VT_TRANSPOSE, K_COUNT
 };
 const char *kKernelNames[K_COUNT] = {"metadata_upload", "main_fwd", "branch_local_fwd", "lse_merge",
                                      "bwd_preprocess", "main_bwd_dq", "main_bwd_dkdv", "branch_local_bwd",
-                                     "dq_convert"};
+                                     "dq_convert",      "vt_transpose"};
 
 struct TimingState {
   std::mutex mu;
@@ -91,6 +91,7 @@ Meta make_meta(const ba_plan *pl, const void *ws) {
   m.group_heads = reinterpret_cast<const int32_t *>(b + L.group_heads);
   m.qtiles = reinterpret_cast<const QTile *>(b + L.qtiles);
   m.fwd_order = reinterpret_cast<const int32_t *>(b + L.fwd_order);
+  m.fwd_pairs = reinterpret_cast<const int32_t *>(b + L.fwd_pairs);
   m.tile_row_id = reinterpret_cast<const int32_t *>(b + L.tile_row_id);
   m.tile_row_end = reinterpret_cast<const int32_t *>(b + L.tile_row_end);
   m.row_lo = reinterpret_cast<const int32_t *>(b + L.row_lo);
@@ -99,6 +100,8 @@ Meta make_meta(const ba_plan *pl, const void *ws) {
   m.mode = reinterpret_cast<const int32_t *>(b + L.mode);
   m.ktiles = reinterpret_cast<const KTile *>(b + L.ktiles);
   m.bwd_order = reinterpret_cast<const int32_t *>(b + L.bwd_order);
+  m.vt_tiles = reinterpret_cast<const int32_t *>(b + L.vt_tiles);
+  m.vt_base = reinterpret_cast<const int32_t *>(b + L.vt_base);
   m.N = pl->N;
   m.Nq = pl->Nq;
   m.Rb = pl->Rb;
@@ -110,6 +113,8 @@ Meta make_meta(const ba_plan *pl, const void *ws) {
   m.rows_per_tile = pl->rows_per_tile;
   m.n_qtiles = pl->n_qtiles;
   m.n_ktiles = pl->n_ktiles;
+  m.n_fwd_pairs = pl->n_fwd_pairs;
+  m.n_vt_tiles = pl->n_vt_tiles;
   m.scale = pl->scale;
   return m;
 }
@@ -150,16 +155,24 @@ ba_status_t upload(const ba_plan *pl, void *ws, hipStream_t st) {
 #define BA_HIP(x, what) BA_TRY(hip_status((x), what))
 
 ba_status_t run_main_fwd(const ba_plan *pl, const Meta &mt, const void *q, const void *qb, const void *k,
-                         const void *v, void *o, float *lse, float *o_pre, float *lse_pre, hipStream_t st) {
-  Timed tm(K_MAIN_FWD, st);
-  if (pl->dtype == BA_BF16)
-    BA_HIP(launch_main_fwd_bf16(mt, (const bf16 *)q, (const bf16 *)qb, (const bf16 *)k, (const bf16 *)v, (bf16 *)o,
-                                lse, o_pre, lse_pre, st),
+                         const void *v, void *o, float *lse, float *o_pre, float *lse_pre, void *ws,
+                         hipStream_t st) {
+  if (pl->dtype == BA_BF16) {
+    bf16 *vt = reinterpret_cast<bf16 *>(static_cast<uint8_t *>(ws) + pl->off_vt);
+    {
+      Timed tv(K_VT_TRANSPOSE, st);
+      BA_HIP(launch_vt_transpose_bf16(mt, (const bf16 *)v, vt, st), "V transpose");
+    }
+    Timed tm(K_MAIN_FWD, st);
+    BA_HIP(launch_main_fwd_bf16(mt, (const bf16 *)q, (const bf16 *)qb, (const bf16 *)k, vt, (bf16 *)o, lse, o_pre,
+                                lse_pre, st),
            "main-sequence forward");
-  else
+  } else {
+    Timed tm(K_MAIN_FWD, st);
     BA_HIP(launch_main_fwd_f32(mt, (const float *)q, (const float *)qb, (const float *)k, (const float *)v,
                                (float *)o, lse, o_pre, lse_pre, st),
            "main-sequence forward");
+  }
   return BA_OK;
 }
 
@@ -193,7 +206,7 @@ ba_status_t ba_main_fwd(const ba_plan_t *pl, const void *q, const void *qb, cons
   BA_TRY(check_ws(pl, workspace, ws_bytes, 2));
   hipStream_t st = static_cast<hipStream_t>(stream);
   BA_TRY(upload(pl, workspace, st));
-  return run_main_fwd(pl, make_meta(pl, workspace), q, qb, k, v, o, lse, o_pre, lse_pre, st);
+  return run_main_fwd(pl, make_meta(pl, workspace), q, qb, k, v, o, lse, o_pre, lse_pre, workspace, st);
 }
 
 ba_status_t ba_branch_local_fwd(const ba_plan_t *pl, const void *qb, const void *kb, const void *vb, float *o_loc,
@@ -256,7 +269,7 @@ ba_status_t branch_attn_fwd(const ba_plan_t *pl, const void *q, const void *k, c
   float *lse_pre = reinterpret_cast<float *>(ws + pl->off_lse_pre);
   float *o_loc = reinterpret_cast<float *>(ws + pl->off_o_loc);
   float *lse_loc = reinterpret_cast<float *>(ws + pl->off_lse_loc);
-  BA_TRY(run_main_fwd(pl, mt, q, qb, k, v, o, lse, o_pre, lse_pre, st));
+  BA_TRY(run_main_fwd(pl, mt, q, qb, k, v, o, lse, o_pre, lse_pre, workspace, st));
   BA_TRY(timed(K_BRANCH_LOCAL_FWD, st, "branch-local forward",
                [&] { return launch_branch_local_fwd(mt, pl->dtype, qb, kb, vb, o_loc, lse_loc, st); }));
   BA_TRY(timed(K_LSE_MERGE, st, "lse_merge", [&] {

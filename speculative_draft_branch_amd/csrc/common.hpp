@@ -24,6 +24,7 @@ struct Meta {
   const int32_t *group_heads;
   const QTile *qtiles;
   const int32_t *fwd_order;
+  const int32_t *fwd_pairs;
   const int32_t *tile_row_id;
   const int32_t *tile_row_end;
   const int32_t *row_lo;
@@ -32,9 +33,11 @@ struct Meta {
   const int32_t *mode;
   const KTile *ktiles;
   const int32_t *bwd_order;
+  const int32_t *vt_tiles;
+  const int32_t *vt_base;
   int64_t N, Nq, Rb, A;
   int32_t hq, hkv, G, d, rows_per_tile;
-  int32_t n_qtiles, n_ktiles;
+  int32_t n_qtiles, n_ktiles, n_fwd_pairs, n_vt_tiles;
   float scale;
 };
 
@@ -109,12 +112,51 @@ __device__ __forceinline__ int lds_off(int row, int d) {  // element offset of (
   return row * HD + ((((d >> 3) ^ swz<HD>(row))) << 3) + (d & 7);
 }
 
+// Per-lane addressing of MFMA operand reads from a swizzled [row][HD] bf16 LDS
+// tile. The swizzle XORs chunk-index bits that the k-step (or d-block) index
+// and the lane's own chunk bits never share, so an operand's byte offset is
+// (step << c) ^ t plus a per-lane row base: one xad per read from two
+// registers, instead of one precomputed address register per step.
+//
+// Row read (ds_read_b128, A operand with k = d): lane reads row
+// 32*blk + r (r = lane % 32 plus a caller offset), chunk 2*ks + lane/32.
+template <int HD>
+__device__ __forceinline__ void row_read_init(int r, int lane, uint32_t &base, uint32_t &t) {
+  base = (uint32_t)(r * HD * 2);
+  t = (uint32_t)((lane >> 5) ^ swz<HD>(r)) << 4;
+}
+template <int HD>
+__device__ __forceinline__ bf16x8 row_read(const bf16 *tile, uint32_t base, uint32_t t, int blk, int ks) {
+  const uint32_t off = base + (((uint32_t)ks << 5) ^ t) + (uint32_t)(blk * 32 * HD * 2);
+  return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(tile) + off);
+}
+// Transposing read (ds_read_b64_tr_b16, operand with k = row): the 16-lane
+// group g = lane/16 reads rows 16*kk + 4*(g/2) + (lane%16)/4 + 8c, d = 32*dt +
+// 16*(g%2) + 4*(lane%4) .. +3; one (base, t) pair per c.
+template <int HD>
+__device__ __forceinline__ void tr_read_init(int lane, int c, uint32_t &base, uint32_t &t) {
+  const int g = lane >> 4, in_j = (lane & 15) >> 2, in_q = lane & 3;
+  const int row = 4 * (g >> 1) + in_j + 8 * c;
+  const int cl = (g & 1) * 2 + (in_q >> 1);  // chunk within a 32-wide d block
+  base = (uint32_t)(row * HD * 2 + 8 * (in_q & 1));
+  t = (uint32_t)(cl ^ swz<HD>(row)) << 4;
+}
+
 // Transposed LDS read (gfx950 ds_read_b64_tr_b16): within each 16-lane group,
 // output lane i, slot j takes element (i % 4) of the 8 bytes addressed by input
 // lane 4j + i/4.
 __device__ __forceinline__ i16x4 lds_read_tr(const bf16 *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
 }
+template <int HD>
+__device__ __forceinline__ i16x4 tr_read(const bf16 *tile, uint32_t base, uint32_t t, int kk, int dt) {
+  const uint32_t off = base + (((uint32_t)dt << 6) ^ t) + (uint32_t)(kk * 16 * HD * 2);
+  return lds_read_tr(reinterpret_cast<const bf16 *>(reinterpret_cast<const char *>(tile) + off));
+}
+// Makes the compiler treat a per-lane address term as freshly produced, so the
+// addresses derived from it are recomputed where they are used (one VALU op per
+// read) rather than hoisted into one live register per read.
+__device__ __forceinline__ void opaque(uint32_t &x) { asm volatile("" : "+v"(x)); }
 
 // Stage rows [k0, k0 + ROWS) of a [rows, Hkv, HD] bf16 tensor (kv head g) into
 // an LDS tile in the swizzled layout; rows past `last` (inclusive bound) are

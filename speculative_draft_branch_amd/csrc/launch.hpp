@@ -25,7 +25,10 @@ hipError_t launch_main_bwd_f32(const Meta &mt, const float *q, const float *qb, 
                                const float *d_o, const float *d_ob, const float *lse, const float *lseb,
                                const float *delta, float *dq_acc, float *dk, float *dv, hipStream_t st);
 // bf16 MFMA main-sequence kernels
-hipError_t launch_main_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *v,
+// V^T tiles of each sequence: [tile][Hkv][d][64 keys], keys of each 16-key group
+// stored in MFMA operand-slot order; keys past the sequence end are zero.
+hipError_t launch_vt_transpose_bf16(const Meta &mt, const bf16 *v, bf16 *vt, hipStream_t st);
+hipError_t launch_main_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *vt,
                                 bf16 *o, float *lse, float *o_pre, float *lse_pre, hipStream_t st);
 hipError_t launch_main_bwd_dq_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *v,
                                    const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,

@@ -13,8 +13,9 @@
 //    lane; dQ^T += K^T dS^T takes K through the transposing LDS read and dS^T
 //    straight from registers. dQ is written once per row (float32, into the
 //    accumulator the branch-local backward adds to).
-//  * dkdv: key-tile major: 128 main keys of one kv head against every query
-//    tile whose rows may see them; each wave owns 32 keys and keeps their dK, dV
+//  * dkdv: key-tile major: 256 main keys of one kv head (four waves of 64
+//    keys, sharing every staged query tile) against every query tile whose rows
+//    may see them; each wave owns 64 keys and keeps their dK, dV
 //    in registers across all query tiles, written once, summed over the group's
 //    q heads. S = Q K^T puts the key on the lane, so P and dS are directly the
 //    A operands of dV += P^T dO and dK += dS^T Q (dO and Q via the transposing
@@ -272,60 +273,87 @@ __global__ __launch_bounds__(256) void bwd_gather_bf16_kernel(Meta mt, const bf1
 
 namespace {
 
-template <int HD>
+// Keys per wave: KB blocks of 32; eight waves of one block each give two waves
+// per SIMD within the 256-register budget (K, V fragments and the dK, dV
+// accumulators alone hold 192 registers at d = 128).
+constexpr int kDkdvBlocks = 1;
+constexpr int kDkdvThreads = 64 * kBwdKeys / (32 * kDkdvBlocks);
+
+template <int HD, int KB>
 struct DkdvState {
   static constexpr int KS = HD / 16;
   static constexpr int DT = HD / 32;
-  bf16x8 kf[KS], vf[KS];
-  f32x16 adk[DT], adv[DT];
-  int my_key, wkey_lo, key_hi;
+  bf16x8 kf[KB][KS], vf[KB][KS];
+  f32x16 adk[KB][DT], adv[KB][DT];
+  int my_key[KB];
+  int wkey_lo, key_hi;
   int grp, in_j, in_q, lane;
 };
 
-// One query tile (128 MFMA rows staged in LDS) against the wave's 32 keys.
-template <int HD>
-__device__ __forceinline__ void dkdv_tile(DkdvState<HD> &st, const bf16 *sQ, const bf16 *sdO, const float *sL2,
+// Rows of one staged query tile against the wave's 32*KB keys; MASK when some
+// row's prefix end or the key range cuts through the wave's keys.
+template <int HD, int KB, bool MASK>
+__device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ, const bf16 *sdO, const float *sL2,
                                           const float *sD, const int *sEnd, float sl2) {
   constexpr int BM = kTileRows;
-  constexpr int KS = DkdvState<HD>::KS, DT = DkdvState<HD>::DT;
+  constexpr int KS = DkdvState<HD, KB>::KS, DT = DkdvState<HD, KB>::DT;
   const int lane = st.lane;
-  const int end_min = uni(sEnd[BM]), end_max = uni(sEnd[BM + 1]), valid_rows = uni(sEnd[BM + 2]);
-  if (end_max < st.wkey_lo || st.wkey_lo >= st.key_hi) return;  // no row of this tile sees the wave's keys
-  const bool need_mask = end_min < st.wkey_lo + 31 || st.wkey_lo + 31 >= st.key_hi || valid_rows < BM;
-  // S and dP of row block rb (rows 32rb..32rb+31) x the wave's 32 keys.
-  auto scores = [&](int rb, f32x16 &s, f32x16 &dp) {
-    s = f32x16{};
-    dp = f32x16{};
-    const int ar = rb * 32 + (lane & 31);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int off = ar * HD + (((2 * ks + (lane >> 5)) ^ swz<HD>(ar)) << 3);
-      s = mfma32(*reinterpret_cast<const bf16x8 *>(sQ + off), st.kf[ks], s);
-      dp = mfma32(*reinterpret_cast<const bf16x8 *>(sdO + off), st.vf[ks], dp);
-    }
-  };
-  // Software-pipelined over the row blocks: the S/dP products of block rb+1
-  // are issued before block rb's exponentials, so MFMA and VALU work overlap.
-  f32x16 s_nx, dp_nx;
-  scores(0, s_nx, dp_nx);
-#pragma unroll
+#pragma unroll 1
   for (int rb = 0; rb < BM / 32; ++rb) {
-    const f32x16 s = s_nx, dp = dp_nx;
-    if (rb + 1 < BM / 32) scores(rb + 1, s_nx, dp_nx);
-    // element i: row rb*32 + (i/4)*8 + 4*(lane/32) + i%4, key my_key
-    bf16x8 pa[2], dsa[2];
+    // Rows 32rb..32rb+31: S first, turned into P (kept as the bf16 operand of
+    // dV, which also serves dS), then dP, so only one score block is live.
+    // element i: row rb*32 + (i/4)*8 + 4*(lane/32) + i%4, key my_key[b]
+    const int ar = rb * 32 + (lane & 31);
+    bf16x8 pa[KB][2], dsa[KB][2];
+    {
+      f32x16 sc[KB];
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int r0 = rb * 32 + i4 * 8 + 4 * (lane >> 5);
-      const f32x4 l2 = *reinterpret_cast<const f32x4 *>(sL2 + r0);
-      const f32x4 dd = *reinterpret_cast<const f32x4 *>(sD + r0);
+      for (int b = 0; b < KB; ++b) sc[b] = f32x16{};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = i4 * 4 + e;
-        float p = fast_exp2(fmaf(s[i], sl2, -l2[e]));
-        if (need_mask && (sEnd[r0 + e] < st.my_key || st.my_key >= st.key_hi)) p = 0.0f;
-        pa[i >> 3][i & 7] = (bf16)p;
-        dsa[i >> 3][i & 7] = (bf16)(p * (dp[i] - dd[e]));
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(sQ + ar * HD + (((2 * ks + (lane >> 5)) ^ swz<HD>(ar)) << 3));
+#pragma unroll
+        for (int b = 0; b < KB; ++b) sc[b] = mfma32(aq, st.kf[b][ks], sc[b]);
+      }
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int r0 = rb * 32 + i4 * 8 + 4 * (lane >> 5);
+        const f32x4 l2 = *reinterpret_cast<const f32x4 *>(sL2 + r0);
+        int4 ends = {0, 0, 0, 0};
+        if constexpr (MASK) ends = *reinterpret_cast<const int4 *>(sEnd + r0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i4 * 4 + e;
+#pragma unroll
+          for (int b = 0; b < KB; ++b) {
+            float p = fast_exp2(fmaf(sc[b][i], sl2, -l2[e]));
+            if (MASK && (ends[e] < st.my_key[b] || st.my_key[b] >= st.key_hi)) p = 0.0f;
+            pa[b][i >> 3][i & 7] = (bf16)p;
+          }
+        }
+      }
+    }
+    {
+      f32x16 dp[KB];
+#pragma unroll
+      for (int b = 0; b < KB; ++b) dp[b] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ao = *reinterpret_cast<const bf16x8 *>(sdO + ar * HD + (((2 * ks + (lane >> 5)) ^ swz<HD>(ar)) << 3));
+#pragma unroll
+        for (int b = 0; b < KB; ++b) dp[b] = mfma32(ao, st.vf[b][ks], dp[b]);
+      }
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int r0 = rb * 32 + i4 * 8 + 4 * (lane >> 5);
+        const f32x4 dd = *reinterpret_cast<const f32x4 *>(sD + r0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i4 * 4 + e;
+#pragma unroll
+          for (int b = 0; b < KB; ++b)
+            dsa[b][i >> 3][i & 7] = (bf16)((float)pa[b][i >> 3][i & 7] * (dp[b][i] - dd[e]));
+        }
       }
     }
     // dV += P^T dO, dK += dS^T Q over these 32 rows (two 16-row k-steps).
@@ -338,27 +366,45 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<HD> &st, const bf16 *sQ, con
         const int d = dt * 32 + (st.grp & 1) * 16 + 4 * st.in_q;
         const bf16x8 bo = join(lds_read_tr(sdO + lds_off<HD>(row0, d)), lds_read_tr(sdO + lds_off<HD>(row0 + 8, d)));
         const bf16x8 bq = join(lds_read_tr(sQ + lds_off<HD>(row0, d)), lds_read_tr(sQ + lds_off<HD>(row0 + 8, d)));
-        st.adv[dt] = mfma32(pa[kh], bo, st.adv[dt]);
-        st.adk[dt] = mfma32(dsa[kh], bq, st.adk[dt]);
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+          st.adv[b][dt] = mfma32(pa[b][kh], bo, st.adv[b][dt]);
+          st.adk[b][dt] = mfma32(dsa[b][kh], bq, st.adk[b][dt]);
+        }
       }
     }
   }
 }
 
+// One query tile (128 MFMA rows staged in LDS) against the wave's 32*KB keys.
+template <int HD, int KB>
+__device__ __forceinline__ void dkdv_tile(DkdvState<HD, KB> &st, const bf16 *sQ, const bf16 *sdO, const float *sL2,
+                                          const float *sD, const int *sEnd, float sl2) {
+  constexpr int BM = kTileRows;
+  constexpr int WK = 32 * KB;  // keys of this wave
+  const int end_min = uni(sEnd[BM]), end_max = uni(sEnd[BM + 1]), valid_rows = uni(sEnd[BM + 2]);
+  if (end_max < st.wkey_lo || st.wkey_lo >= st.key_hi) return;  // no row of this tile sees the wave's keys
+  if (end_min < st.wkey_lo + WK - 1 || st.wkey_lo + WK - 1 >= st.key_hi || valid_rows < BM)
+    dkdv_rows<HD, KB, true>(st, sQ, sdO, sL2, sD, sEnd, sl2);
+  else
+    dkdv_rows<HD, KB, false>(st, sQ, sdO, sL2, sD, sEnd, sl2);
+}
+
 }  // namespace
 
 template <int HD>
-__global__ __launch_bounds__(256) void main_bwd_dkdv_bf16_kernel(Meta mt, const bf16 *__restrict__ k,
-                                                                 const bf16 *__restrict__ v,
-                                                                 const bf16 *__restrict__ qt_rows,
-                                                                 const bf16 *__restrict__ do_rows,
-                                                                 const float *__restrict__ lt,
-                                                                 const float *__restrict__ dtt,
-                                                                 const int *__restrict__ et,
-                                                                 bf16 *__restrict__ dk, bf16 *__restrict__ dv) {
+__global__ __launch_bounds__(kDkdvThreads, 1) void main_bwd_dkdv_bf16_kernel(Meta mt, const bf16 *__restrict__ k,
+                                                                          const bf16 *__restrict__ v,
+                                                                          const bf16 *__restrict__ qt_rows,
+                                                                          const bf16 *__restrict__ do_rows,
+                                                                          const float *__restrict__ lt,
+                                                                          const float *__restrict__ dtt,
+                                                                          const int *__restrict__ et,
+                                                                          bf16 *__restrict__ dk, bf16 *__restrict__ dv) {
   constexpr int BM = kTileRows;  // 128 MFMA rows per query tile
+  constexpr int KB = kDkdvBlocks, NT = kDkdvThreads;
   constexpr int KS = HD / 16, DT = HD / 32;
-  static_assert(kBwdKeys == 128 && BM == 128, "tile shape");
+  static_assert(kBwdKeys == 32 * KB * (NT / 64) && BM == 128, "tile shape");
   __shared__ __attribute__((aligned(16))) bf16 sQ0[BM * HD];
   __shared__ __attribute__((aligned(16))) bf16 sO0[BM * HD];
   __shared__ __attribute__((aligned(16))) bf16 sQ1[BM * HD];
@@ -373,7 +419,7 @@ __global__ __launch_bounds__(256) void main_bwd_dkdv_bf16_kernel(Meta mt, const 
   const float sl2 = mt.scale * kLog2e;
 
   // Query tile qi, kv head g -> one LDS buffer (all asynchronous).
-  AsyncTile<HD, BM, 256> rowt;
+  AsyncTile<HD, BM, NT> rowt;
   rowt.init(HD, tid);
   auto prefetch = [&](int qi, bf16 *sQ, bf16 *sO, float *sL, float *sD, int *sE) {
     const int64_t tb = ((int64_t)qi * hkv + g) * BM;
@@ -385,27 +431,30 @@ __global__ __launch_bounds__(256) void main_bwd_dkdv_bf16_kernel(Meta mt, const 
   };
   if (kt.qt_begin < kt.qt_end) prefetch(kt.qt_begin, sQ0, sO0, sL0, sD0, sE0);
 
-  // The wave's own K and V as B operands: lane holds key 32*wave + lane%32,
-  // d = 16*ks + 8*(lane/32) + 0..7.
-  DkdvState<HD> st;
-  st.my_key = kt.key_lo + wave * 32 + (lane & 31);
-  st.wkey_lo = kt.key_lo + wave * 32;
+  // The wave's own K and V as B operands: in key block b, lane holds key
+  // 32*(KB*wave + b) + lane%32, d = 16*ks + 8*(lane/32) + 0..7.
+  DkdvState<HD, KB> st;
+  st.wkey_lo = kt.key_lo + wave * 32 * KB;
   st.key_hi = kt.key_hi;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if (st.my_key < kt.key_hi) {
-      const int64_t src = ((int64_t)st.my_key * hkv + g) * HD + 16 * ks + 8 * (lane >> 5);
-      st.kf[ks] = *reinterpret_cast<const bf16x8 *>(k + src);
-      st.vf[ks] = *reinterpret_cast<const bf16x8 *>(v + src);
-    } else {
-      st.kf[ks] = bf16x8{};
-      st.vf[ks] = bf16x8{};
-    }
-  }
+  for (int b = 0; b < KB; ++b) {
+    st.my_key[b] = st.wkey_lo + 32 * b + (lane & 31);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    st.adk[dt] = f32x16{};
-    st.adv[dt] = f32x16{};
+    for (int ks = 0; ks < KS; ++ks) {
+      if (st.my_key[b] < kt.key_hi) {
+        const int64_t src = ((int64_t)st.my_key[b] * hkv + g) * HD + 16 * ks + 8 * (lane >> 5);
+        st.kf[b][ks] = *reinterpret_cast<const bf16x8 *>(k + src);
+        st.vf[b][ks] = *reinterpret_cast<const bf16x8 *>(v + src);
+      } else {
+        st.kf[b][ks] = bf16x8{};
+        st.vf[b][ks] = bf16x8{};
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      st.adk[b][dt] = f32x16{};
+      st.adv[b][dt] = f32x16{};
+    }
   }
   st.lane = lane;
   st.grp = lane >> 4;
@@ -416,28 +465,30 @@ __global__ __launch_bounds__(256) void main_bwd_dkdv_bf16_kernel(Meta mt, const 
     wait_async_loads();
     __syncthreads();  // tile qi is in buffer 0; every wave is done with buffer 1
     if (qi + 1 < kt.qt_end) prefetch(qi + 1, sQ1, sO1, sL1, sD1, sE1);
-    dkdv_tile<HD>(st, sQ0, sO0, sL0, sD0, sE0, sl2);
+    dkdv_tile<HD, KB>(st, sQ0, sO0, sL0, sD0, sE0, sl2);
     if (qi + 1 >= kt.qt_end) break;
     wait_async_loads();
     __syncthreads();  // tile qi+1 is in buffer 1; every wave is done with buffer 0
     if (qi + 2 < kt.qt_end) prefetch(qi + 2, sQ0, sO0, sL0, sD0, sE0);
-    dkdv_tile<HD>(st, sQ1, sO1, sL1, sD1, sE1, sl2);
+    dkdv_tile<HD, KB>(st, sQ1, sO1, sL1, sD1, sE1, sl2);
   }
 
-  // dK, dV of the wave's keys: element i of block dt is key 32*wave +
-  // (i/4)*8 + 4*(lane/32) + i%4, d = 32dt + lane%32.
+  // dK, dV of the wave's keys: element i of block (b, dt) is key wkey_lo +
+  // 32b + (i/4)*8 + 4*(lane/32) + i%4, d = 32dt + lane%32.
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int key = kt.key_lo + wave * 32 + (i >> 2) * 8 + 4 * (lane >> 5) + (i & 3);
-    if (key < kt.key_hi) {
+  for (int b = 0; b < KB; ++b)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int64_t dst = ((int64_t)key * hkv + g) * HD + dt * 32 + (lane & 31);
-        dk[dst] = (bf16)(mt.scale * st.adk[dt][i]);
-        dv[dst] = (bf16)st.adv[dt][i];
+    for (int i = 0; i < 16; ++i) {
+      const int key = st.wkey_lo + 32 * b + (i >> 2) * 8 + 4 * (lane >> 5) + (i & 3);
+      if (key < kt.key_hi) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int64_t dst = ((int64_t)key * hkv + g) * HD + dt * 32 + (lane & 31);
+          dk[dst] = (bf16)(mt.scale * st.adk[b][dt][i]);
+          dv[dst] = (bf16)st.adv[b][dt][i];
+        }
       }
     }
-  }
 }
 
 hipError_t launch_bwd_gather_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *o, const bf16 *ob,
@@ -472,9 +523,9 @@ hipError_t launch_main_bwd_dkdv_bf16(const Meta &mt, const bf16 *k, const bf16 *
   if (mt.n_ktiles == 0) return hipSuccess;
   const unsigned grid = (unsigned)((int64_t)mt.n_ktiles * mt.hkv);
   if (mt.d == 128)
-    main_bwd_dkdv_bf16_kernel<128><<<grid, 256, 0, st>>>(mt, k, v, qt, dot, lt, dtt, et, dk, dv);
+    main_bwd_dkdv_bf16_kernel<128><<<grid, kDkdvThreads, 0, st>>>(mt, k, v, qt, dot, lt, dtt, et, dk, dv);
   else
-    main_bwd_dkdv_bf16_kernel<64><<<grid, 256, 0, st>>>(mt, k, v, qt, dot, lt, dtt, et, dk, dv);
+    main_bwd_dkdv_bf16_kernel<64><<<grid, kDkdvThreads, 0, st>>>(mt, k, v, qt, dot, lt, dtt, et, dk, dv);
   return hipGetLastError();
 }
 

@@ -7,21 +7,29 @@
 // branch attention under context parallelism). Branch K/V never enter these
 // tiles.
 //
-// Work unit: one query tile (up to 128 MFMA rows = base rows x q heads of one
-// kv group, all rows sharing a sequence and sorted by prefix end) against the
-// tile's key range [sequence start, largest prefix end], streamed in 64-key
-// tiles through LDS. Rows that share a prefix end (a main row, the branch rows
-// anchored at the same token, and the q heads of the kv group) share every K/V
-// tile. The grid is longest-first; blockIdx % Hkv selects the kv head, so with
-// 8 kv heads each XCD streams one kv head's keys.
+// Work unit: two query tiles of one sequence that are adjacent in prefix-end
+// order (each up to 128 MFMA rows = base rows x q heads of one kv group, sorted
+// by prefix end) against their key range [sequence start, largest prefix end],
+// streamed in 64-key K/V tiles through LDS. Rows that share a prefix end (a main
+// row, the branch rows anchored at the same token, and the q heads of the kv
+// group) share every K/V tile, and so do the two query tiles. The grid is
+// longest-first; blockIdx % Hkv selects the kv head, so with 8 kv heads each
+// XCD streams one kv head's keys.
 //
-// K/V tiles are double-buffered: global_load_lds writes the next tile straight
-// into LDS while the current one is consumed; one barrier per tile.
+// Eight waves in two groups of four, one group per query tile, two waves per
+// SIMD. Each group alternates a matrix phase (P V of the previous K/V tile, then
+// S of the current one) with a softmax phase, and the groups run one phase
+// apart, separated by workgroup barriers: while one group's exponentials occupy
+// the vector ALUs the other group's MFMAs keep the matrix cores busy. K and V
+// tiles are double-buffered and written straight into LDS by global_load_lds;
+// a tile is requested two phases before its first use.
 //
 // Per wave (32 query rows): S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so each
 // lane owns one query row (lane % 32) and row max/sum need a single exchange
 // between the two wave halves; P^T feeds O^T += V^T P^T straight from
-// registers, with V read from LDS by the transposing ds_read_b64_tr_b16. The
+// registers. V is transposed once per call into 64-key tiles [d][key] whose
+// keys sit in the MFMA operand-slot order, so its operand is a plain 16-byte
+// row read (the transposing LDS read runs at about half that rate). The
 // running max is only raised (and O, l rescaled) when a row's max grows by more
 // than 2^8, which keeps P <= 256 and skips almost every rescale.
 #include <climits>
@@ -42,26 +50,64 @@ struct FwdState {
   f32x16 acc[DT];
   float m_run, l_run;
   int end, wmin, wmax;
-  int grp, in_j, in_q, lane;
+  int lane;
+  uint32_t k_base, k_t;  // K row reads
+  uint32_t v_base, v_t;  // V^T row reads
 };
 
-// One 64-key tile [k0, k0 + 64) of the wave's 32 rows against LDS tiles sK, sV.
-template <int HD>
-__device__ __forceinline__ void fwd_tile(FwdState<HD> &st, const bf16 *sK, const bf16 *sV, int k0, float sl2) {
+// Matrix phase: O^T += V^T P^T for the previous K/V tile (PV), then the raw
+// scores S^T[key][row] of the current tile in two 32-key blocks (S). PV k-step
+// kk covers tile keys 16kk..16kk+15; operand slot 8*half + 4c + j <-> key
+// 16kk + 8c + 4*half + j on both operands, which is the order the V^T tile
+// stores them in, so lane (d, half) reads 8 consecutive elements of row d.
+//
+// The phase is one software pipeline of (LDS read, MFMA) steps: the operands
+// of the next kRing steps are always in flight, so LDS latency is paid about
+// once per phase rather than once per k-step.
+constexpr int kRing = 8;
+
+template <int HD, bool PV, bool S>
+__device__ __forceinline__ void fwd_mphase(FwdState<HD> &st, const bf16 *sVt, const bf16 *sK, const bf16x8 (&pb)[4],
+                                           f32x16 (&s)[2]) {
   constexpr int KS = FwdState<HD>::KS, DT = FwdState<HD>::DT;
-  const int lane = st.lane;
-  // S^T[key][row] for two 32-key blocks.
-  f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int r = kb * 32 + (lane & 31);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int ch = 2 * ks + (lane >> 5);
-      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sK + r * HD + ((ch ^ swz<HD>(r)) << 3));
-      s[kb] = mfma32(a, st.qf[ks], s[kb]);
-    }
+  constexpr int NPV = PV ? 4 * DT : 0;  // step i < NPV: kk = i / DT, dt = i % DT
+  constexpr int NS = S ? 2 * KS : 0;    // then step NPV + j: ks = j / 2, kb = j % 2
+  constexpr int N = NPV + NS;
+  constexpr int R = kRing < N ? kRing : N;
+  auto rd = [&](int i) -> bf16x8 {
+    if (i < NPV) return row_read<64>(sVt, st.v_base, st.v_t, i % DT, i / DT);
+    const int j = i - NPV;
+    return row_read<HD>(sK, st.k_base, st.k_t, j % 2, j / 2);
+  };
+  if constexpr (S) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
   }
+  // The scheduling barriers pin this order; left alone, the compiler sinks
+  // every read next to its MFMA and waits for each one in turn.
+  bf16x8 ring[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) ring[i] = rd(i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i < NPV) {
+      st.acc[i % DT] = mfma32(ring[i % R], pb[i / DT], st.acc[i % DT]);
+    } else {
+      const int j = i - NPV;
+      s[j % 2] = mfma32(ring[i % R], st.qf[j / 2], s[j % 2]);
+    }
+    if (i + R < N) ring[i % R] = rd(i + R);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Softmax phase for the tile [k0, k0 + 64): mask keys past each row's prefix
+// end, raise the running max if needed, and form P^T in bf16.
+template <int HD>
+__device__ __forceinline__ void fwd_softmax(FwdState<HD> &st, f32x16 (&s)[2], int k0, float sl2, bf16x8 (&pb)[4]) {
+  constexpr int DT = FwdState<HD>::DT;
+  const int lane = st.lane;
   if (k0 + 63 > st.wmin) {  // some key of this tile lies past some row's prefix end
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -87,7 +133,6 @@ __device__ __forceinline__ void fwd_tile(FwdState<HD> &st, const bf16 *sK, const
   }
   const float m_use = (st.m_run == -INFINITY) ? 0.0f : st.m_run;
   float rs = 0.0f;
-  bf16x8 pb[4];  // P^T operands of the four 16-key k-steps
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -97,61 +142,69 @@ __device__ __forceinline__ void fwd_tile(FwdState<HD> &st, const bf16 *sK, const
       pb[kb * 2 + (i >> 3)][i & 7] = (bf16)p;
     }
   st.l_run += rs;
-  // O^T += V^T P^T. k-step kk covers tile keys 16kk..16kk+15; operand slot
-  // 8*half + 4c + j <-> key 16kk + 8c + 4*half + j on both operands.
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int key0 = kk * 16 + 4 * (st.grp >> 1) + st.in_j;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = dt * 32 + (st.grp & 1) * 16 + 4 * st.in_q;
-      const i16x4 t0 = lds_read_tr(sV + lds_off<HD>(key0, d));
-      const i16x4 t1 = lds_read_tr(sV + lds_off<HD>(key0 + 8, d));
-      st.acc[dt] = mfma32(join(t0, t1), pb[kk], st.acc[dt]);
-    }
-  }
+}
+
+// Workgroup barrier between phases. The LDS reads of the phase are complete
+// before it (their buffers may be refilled right after); with WAIT_DMA the
+// wave's outstanding LDS DMA is complete too, so after the barrier every
+// requested tile is in LDS. The waits go through the builtin so the compiler's
+// own wait insertion knows about them: otherwise it assumes the DMA into a
+// buffer is still pending when that buffer is next read and waits for every
+// load in flight, including the ones just issued for later tiles. The empty
+// asm statements keep the compiler from moving memory accesses across.
+template <bool WAIT_DMA>
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+  if constexpr (WAIT_DMA)
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  else
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 }  // namespace
 
 template <int HD>
-__global__ __launch_bounds__(256, 2) void main_fwd_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
+__global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
                                                             const bf16 *__restrict__ qb,
                                                             const bf16 *__restrict__ k,
-                                                            const bf16 *__restrict__ v, bf16 *__restrict__ o,
+                                                            const bf16 *__restrict__ vt, bf16 *__restrict__ o,
                                                             float *__restrict__ lse, float *__restrict__ o_pre,
                                                             float *__restrict__ lse_pre) {
   constexpr int BN = 64;  // keys per K/V tile
   constexpr int KS = HD / 16, DT = HD / 32;
   __shared__ __attribute__((aligned(16))) bf16 sK0[BN * HD];
-  __shared__ __attribute__((aligned(16))) bf16 sV0[BN * HD];
   __shared__ __attribute__((aligned(16))) bf16 sK1[BN * HD];
+  __shared__ __attribute__((aligned(16))) bf16 sV0[BN * HD];
   __shared__ __attribute__((aligned(16))) bf16 sV1[BN * HD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grpi = wave >> 2;  // ping-pong group: 0 runs one phase ahead of 1
   const int hkv = mt.hkv, G = mt.G;
   const int g = blockIdx.x % hkv;
-  const QTile tile = load_qtile(mt.qtiles + uni(mt.fwd_order[blockIdx.x / hkv]));
-  const int kv_lo = tile.kv_lo, kv_end = tile.end_max;
+  const int pair = blockIdx.x / hkv;
+  const int ta = uni(mt.fwd_pairs[2 * pair]), tb = uni(mt.fwd_pairs[2 * pair + 1]);
+  const QTile tile_a = load_qtile(mt.qtiles + ta);
+  const int end_b = tb >= 0 ? uni(mt.qtiles[tb].end_max) : -1;
+  const int kv_lo = tile_a.kv_lo, kv_end = max(tile_a.end_max, end_b);
   const int ntiles = (kv_end - kv_lo + BN) / BN;
 
-  // Start fetching the first K/V tile before anything else. K and V share the
-  // layout, so one set of per-lane offsets serves both.
-  AsyncTile<HD, BN, 256> kvt;
-  kvt.init(hkv * HD, tid);
-  const bf16 *kg = k + (int64_t)g * HD, *vg = v + (int64_t)g * HD;
-  kvt.load(sK0, kg, kv_lo, kv_end);
-  kvt.load(sV0, vg, kv_lo, kv_end);
-
-  // This lane's query row: MFMA row 32*wave + lane%32 = base row * G + head.
+  // This lane's query row: MFMA row 32*(wave%4) + lane%32 = base row * G + head
+  // of the group's tile.
   FwdState<HD> st;
-  const int mrow = wave * 32 + (lane & 31);
+  const int mrow = (wave & 3) * 32 + (lane & 31);
   const int bi = mrow / G, hj = mrow - bi * G;
   int row = -1;
   st.end = -1;
-  if (bi < tile.nrows) {
-    row = mt.tile_row_id[tile.row_begin + bi];
-    st.end = mt.tile_row_end[tile.row_begin + bi];
+  const int my_tile = grpi ? tb : ta;
+  if (my_tile >= 0) {
+    const QTile tile = load_qtile(mt.qtiles + my_tile);
+    if (bi < tile.nrows) {
+      row = mt.tile_row_id[tile.row_begin + bi];
+      st.end = mt.tile_row_end[tile.row_begin + bi];
+    }
   }
   const int h = mt.group_heads[g * G + hj];
   const bool is_main = row >= 0 && row < mt.Nq;
@@ -174,31 +227,62 @@ __global__ __launch_bounds__(256, 2) void main_fwd_bf16_kernel(Meta mt, const bf
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) st.acc[dt] = f32x16{};
   st.lane = lane;
-  st.grp = lane >> 4;
-  st.in_j = (lane & 15) >> 2;
-  st.in_q = lane & 3;
+  row_read_init<HD>(lane & 31, lane, st.k_base, st.k_t);
+  row_read_init<64>(lane & 31, lane, st.v_base, st.v_t);
   const float sl2 = mt.scale * kLog2e;
 
-  // Tiles alternate between the two buffers; the loop is unrolled by two so
-  // each buffer is a distinct LDS object.
-  for (int j = 0; j < ntiles; j += 2) {
-    const int k0 = kv_lo + j * BN;
-    wait_async_loads();
-    __syncthreads();  // tile j is in buffer 0; every wave is done with buffer 1
-    if (j + 1 < ntiles) {
-      kvt.load(sK1, kg, k0 + BN, kv_end);
-      kvt.load(sV1, vg, k0 + BN, kv_end);
+  // K tiles: 64 keys x d from the [N][Hkv][d] tensor; V^T tiles: d rows x 64
+  // keys, whole tiles of this sequence's transposed copy.
+  AsyncTile<HD, BN, 512> kt;
+  kt.init(hkv * HD, tid);
+  AsyncTile<64, HD, 512> vtt;
+  vtt.init(64, tid);
+  const bf16 *kg = k + (int64_t)g * HD;
+  const bf16 *vtg = vt + ((int64_t)mt.vt_base[tile_a.seq] * hkv + g) * (HD * 64);
+  const int64_t vt_stride = (int64_t)hkv * HD * 64;  // between consecutive V^T tiles
+  kt.load(sK0, kg, kv_lo, kv_end);
+  phase_barrier<true>();
+
+  // Phase slots: slot t runs, for group grpi, local phase u = t - grpi; even u
+  // is the matrix phase of tile j = u/2 (P V of tile j-1, S of tile j), odd u
+  // the softmax of tile (u-1)/2. Tile j's K is in buffer j%2 from slot 2j, its
+  // V in buffer j%2 from slot 2j+2; both are requested at slot 2j-2 and 2j
+  // respectively, so every DMA has two phases to land. The loop is unrolled
+  // over the tile parity so each buffer is a distinct LDS object.
+  f32x16 s[2];
+  bf16x8 pb[4];
+  const int nslots = 2 * ntiles + 2;
+  for (int j = 0;; j += 2) {
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int jj = j + par;  // tile whose matrix phase falls in these two slots
+      bf16 *const sKc = par ? sK1 : sK0, *const sKn = par ? sK0 : sK1;
+      bf16 *const sVc = par ? sV1 : sV0, *const sVp = par ? sV0 : sV1;
+      // slot 2jj: requests, then group 0 matrix phase of jj, group 1 softmax of jj-1
+      if (2 * jj >= nslots) goto done;
+      if (jj + 1 < ntiles) kt.load(sKn, kg, kv_lo + (jj + 1) * BN, kv_end);
+      if (jj < ntiles) vtt.load(sVc, vtg + jj * vt_stride, 0, HD - 1);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        if (h2 == 1 && 2 * jj + 1 >= nslots) goto done;
+        if (grpi == h2) {  // matrix phase of tile jj
+          const bool do_pv = jj >= 1 && jj <= ntiles && kv_lo + (jj - 1) * BN <= st.wmax;
+          const bool do_s = jj < ntiles && kv_lo + jj * BN <= st.wmax;
+          __builtin_amdgcn_s_setprio(1);  // the matrix wave wins issue arbitration over the softmax wave
+          if (do_pv && do_s) fwd_mphase<HD, true, true>(st, sVp, sKc, pb, s);
+          else if (do_s) fwd_mphase<HD, false, true>(st, sVp, sKc, pb, s);
+          else if (do_pv) fwd_mphase<HD, true, false>(st, sVp, sKc, pb, s);
+          __builtin_amdgcn_s_setprio(0);
+        } else {  // softmax of tile jj - 1 (group 1 at h2 = 0) or jj (group 0 at h2 = 1)
+          const int js = jj - 1 + h2;
+          if (js >= 0 && js < ntiles && kv_lo + js * BN <= st.wmax) fwd_softmax<HD>(st, s, kv_lo + js * BN, sl2, pb);
+        }
+        if (h2 == 0) phase_barrier<false>();
+        else phase_barrier<true>();
+      }
     }
-    if (k0 <= st.wmax) fwd_tile<HD>(st, sK0, sV0, k0, sl2);
-    if (j + 1 >= ntiles) break;
-    wait_async_loads();
-    __syncthreads();  // tile j+1 is in buffer 1; every wave is done with buffer 0
-    if (j + 2 < ntiles) {
-      kvt.load(sK0, kg, k0 + 2 * BN, kv_end);
-      kvt.load(sV0, vg, k0 + 2 * BN, kv_end);
-    }
-    if (k0 + BN <= st.wmax) fwd_tile<HD>(st, sK1, sV1, k0 + BN, sl2);
   }
+done:
 
   const float l_tot = half_sum(st.l_run);
   if (row >= 0) {
@@ -225,14 +309,60 @@ __global__ __launch_bounds__(256, 2) void main_fwd_bf16_kernel(Meta mt, const bf
   }
 }
 
-hipError_t launch_main_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *v,
-                                bf16 *o, float *lse, float *o_pre, float *lse_pre, hipStream_t st) {
-  if (mt.n_qtiles == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((int64_t)mt.n_qtiles * mt.hkv);
+// V^T tile: 64 keys of one sequence (zero past its end) x d, written as d rows
+// of 64 keys with bits 2 and 3 of the key index swapped inside each 16-key
+// group (stored position 8h + 4c + j holds key 8c + 4h + j).
+template <int HD>
+__global__ __launch_bounds__(256) void vt_transpose_bf16_kernel(Meta mt, const bf16 *__restrict__ v,
+                                                                bf16 *__restrict__ vt) {
+  constexpr int NCH = HD / 8;
+  constexpr int LD = HD + 2;  // padded LDS row (elements) against bank conflicts on the column reads
+  __shared__ __attribute__((aligned(16))) bf16 t[64 * LD];
+  const int hkv = mt.hkv, g = blockIdx.x % hkv, ti = blockIdx.x / hkv;
+  const int key_lo = mt.vt_tiles[2 * ti], key_hi = mt.vt_tiles[2 * ti + 1];
+  for (int c = threadIdx.x; c < 64 * NCH; c += 256) {
+    const int r = c / NCH, ch = c % NCH;
+    uint4 x = {0u, 0u, 0u, 0u};
+    if (key_lo + r < key_hi) x = *reinterpret_cast<const uint4 *>(v + ((int64_t)(key_lo + r) * hkv + g) * HD + ch * 8);
+    uint32_t *d32 = reinterpret_cast<uint32_t *>(t + r * LD + ch * 8);
+    d32[0] = x.x;
+    d32[1] = x.y;
+    d32[2] = x.z;
+    d32[3] = x.w;
+  }
+  __syncthreads();
+  bf16 *dst = vt + ((int64_t)ti * hkv + g) * (HD * 64);
+  for (int c = threadIdx.x; c < HD * 8; c += 256) {
+    const int d = c >> 3, p8 = c & 7;
+    bf16x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int p = 8 * p8 + e;
+      const int key = (p & ~15) | (p & 3) | ((p & 4) << 1) | ((p & 8) >> 1);
+      out[e] = t[key * LD + d];
+    }
+    *reinterpret_cast<bf16x8 *>(dst + d * 64 + 8 * p8) = out;
+  }
+}
+
+hipError_t launch_vt_transpose_bf16(const Meta &mt, const bf16 *v, bf16 *vt, hipStream_t st) {
+  if (mt.n_vt_tiles == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((int64_t)mt.n_vt_tiles * mt.hkv);
   if (mt.d == 128)
-    main_fwd_bf16_kernel<128><<<grid, 256, 0, st>>>(mt, q, qb, k, v, o, lse, o_pre, lse_pre);
+    vt_transpose_bf16_kernel<128><<<grid, 256, 0, st>>>(mt, v, vt);
   else
-    main_fwd_bf16_kernel<64><<<grid, 256, 0, st>>>(mt, q, qb, k, v, o, lse, o_pre, lse_pre);
+    vt_transpose_bf16_kernel<64><<<grid, 256, 0, st>>>(mt, v, vt);
+  return hipGetLastError();
+}
+
+hipError_t launch_main_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *vt,
+                                bf16 *o, float *lse, float *o_pre, float *lse_pre, hipStream_t st) {
+  if (mt.n_fwd_pairs == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv);
+  if (mt.d == 128)
+    main_fwd_bf16_kernel<128><<<grid, 512, 0, st>>>(mt, q, qb, k, vt, o, lse, o_pre, lse_pre);
+  else
+    main_fwd_bf16_kernel<64><<<grid, 512, 0, st>>>(mt, q, qb, k, vt, o, lse, o_pre, lse_pre);
   return hipGetLastError();
 }
 

@@ -210,6 +210,33 @@ void build(ba_plan *pl) {
     return ca > cb;
   });
 
+  // Forward workgroups take two consecutive tiles of one sequence (their prefix
+  // ends are adjacent in the sorted order, so they share almost every K/V tile);
+  // cost is the longer key range of the two.
+  std::vector<int32_t> fwd_pairs;
+  std::vector<int64_t> pair_cost;
+  for (int32_t s = 0; s < pl->S; ++s) {
+    for (int32_t a = seq_qt_begin[s]; a < seq_qt_begin[s + 1]; a += 2) {
+      const int32_t b = a + 1 < seq_qt_begin[s + 1] ? a + 1 : -1;
+      fwd_pairs.push_back(a);
+      fwd_pairs.push_back(b);
+      const int32_t e = b >= 0 ? std::max(qt[a].end_max, qt[b].end_max) : qt[a].end_max;
+      pair_cost.push_back((int64_t)e - qt[a].kv_lo + 1);
+    }
+  }
+  pl->n_fwd_pairs = (int32_t)pair_cost.size();
+  {
+    std::vector<int32_t> ord(pair_cost.size());
+    std::iota(ord.begin(), ord.end(), 0);
+    std::stable_sort(ord.begin(), ord.end(), [&](int32_t x, int32_t y) { return pair_cost[x] > pair_cost[y]; });
+    std::vector<int32_t> sorted(fwd_pairs.size());
+    for (size_t i = 0; i < ord.size(); ++i) {
+      sorted[2 * i] = fwd_pairs[2 * (size_t)ord[i]];
+      sorted[2 * i + 1] = fwd_pairs[2 * (size_t)ord[i] + 1];
+    }
+    fwd_pairs.swap(sorted);
+  }
+
   // Backward key tiles: per sequence, kBwdKeys main keys each; the query tiles
   // that see a key tile are the sequence's tiles whose largest end reaches it.
   std::vector<KTile> kt;
@@ -239,6 +266,18 @@ void build(ba_plan *pl) {
   std::stable_sort(bwd_order.begin(), bwd_order.end(),
                    [&](int32_t a, int32_t b) { return kt_cost[a] > kt_cost[b]; });
 
+  // Transposed V tiles for the bf16 forward: 64 keys each, aligned to each
+  // sequence's start like the forward's K/V tiles.
+  std::vector<int32_t> vt_tiles, vt_base(pl->S, 0);
+  for (int32_t s = 0; s < pl->S; ++s) {
+    vt_base[s] = (int32_t)(vt_tiles.size() / 2);
+    for (int32_t k0 = pl->cu[s]; k0 < pl->cu[s + 1]; k0 += 64) {
+      vt_tiles.push_back(k0);
+      vt_tiles.push_back(pl->cu[s + 1]);
+    }
+  }
+  pl->n_vt_tiles = (int32_t)(vt_tiles.size() / 2);
+
   // Device metadata blob.
   std::vector<int32_t> mode32(pl->mode.begin(), pl->mode.end());
   std::vector<uint8_t> &blob = pl->blob;
@@ -248,6 +287,7 @@ void build(ba_plan *pl) {
   L.group_heads = put(blob, cur, pl->group_heads);
   L.qtiles = put(blob, cur, qt);
   L.fwd_order = put(blob, cur, fwd_order);
+  L.fwd_pairs = put(blob, cur, fwd_pairs);
   L.tile_row_id = put(blob, cur, trow_id);
   L.tile_row_end = put(blob, cur, trow_end);
   L.row_lo = put(blob, cur, row_lo);
@@ -256,16 +296,21 @@ void build(ba_plan *pl) {
   L.mode = put(blob, cur, mode32);
   L.ktiles = put(blob, cur, kt);
   L.bwd_order = put(blob, cur, bwd_order);
+  L.vt_tiles = put(blob, cur, vt_tiles);
+  L.vt_base = put(blob, cur, vt_base);
   L.total = cur;
   blob.resize(std::max<size_t>(cur, 256));
 
   // Workspace layouts.
   const size_t f32 = sizeof(float);
   size_t base = align_up(blob.size(), 256);
-  pl->ws_split = base;
+  pl->off_vt = base;
+  const size_t vt_bytes =
+      pl->dtype == BA_BF16 ? align_up((size_t)pl->n_vt_tiles * pl->hkv * pl->d * 64 * sizeof(uint16_t), 256) : 0;
+  pl->ws_split = base + vt_bytes;
   size_t o_bytes = align_up((size_t)Rb * pl->hq * pl->d * f32, 256);
   size_t l_bytes = align_up((size_t)Rb * pl->hq * f32, 256);
-  pl->off_o_pre = base;
+  pl->off_o_pre = pl->ws_split;
   pl->off_lse_pre = pl->off_o_pre + o_bytes;
   pl->off_o_loc = pl->off_lse_pre + l_bytes;
   pl->off_lse_loc = pl->off_o_loc + o_bytes;

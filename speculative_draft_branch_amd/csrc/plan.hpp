@@ -14,7 +14,7 @@ namespace ba {
 // Rows per query tile in MFMA rows (base rows x q heads of one kv group).
 constexpr int kTileRows = 128;
 // Keys per backward key tile.
-constexpr int kBwdKeys = 128;
+constexpr int kBwdKeys = 256;
 // Per-query-tile block of row ends the backward gather writes: 128 prefix ends,
 // then the tile's smallest end, largest end and valid MFMA rows (padded to 3 x 64
 // words for whole-wave LDS copies).
@@ -48,6 +48,7 @@ struct BlobLayout {
   size_t group_heads;   // int32 [Hkv * G]: q heads of each kv group
   size_t qtiles;        // QTile [n_qtiles], sequence order
   size_t fwd_order;     // int32 [n_qtiles]: longest-first launch order
+  size_t fwd_pairs;     // int32 [n_fwd_pairs][2]: tiles sharing a forward workgroup (-1 = none), longest first
   size_t tile_row_id;   // int32 [n_qtiles * rows_per_tile]: combined row id, -1 = padding
   size_t tile_row_end;  // int32 [n_qtiles * rows_per_tile]: prefix end of that row
   size_t row_lo;        // int32 [Nq + Rb]: first visible main key of each combined row
@@ -56,6 +57,8 @@ struct BlobLayout {
   size_t mode;          // int32 [A]
   size_t ktiles;        // KTile [n_ktiles]
   size_t bwd_order;     // int32 [n_ktiles]: longest-first launch order
+  size_t vt_tiles;      // int32 [n_vt_tiles][2]: main keys [lo, hi) of each transposed V tile (lo + 64 > hi allowed)
+  size_t vt_base;       // int32 [S]: first transposed V tile of each sequence
   size_t total;
 };
 
@@ -71,12 +74,13 @@ struct ba_plan {
   std::vector<int32_t> cu, q_pos, anchors, cu_branch;
   std::vector<uint8_t> mode;
   int32_t rows_per_tile;  // base rows per query tile
-  int32_t n_qtiles, n_ktiles;
+  int32_t n_qtiles, n_ktiles, n_fwd_pairs, n_vt_tiles;
   int64_t pairs[3];
   ba::BlobLayout layout;
   std::vector<uint8_t> blob;  // host copy of the device metadata
   size_t ws_split, ws_fwd, ws_bwd;
   // workspace regions (byte offsets)
+  size_t off_vt;                                          // forward, bf16: V^T tiles [n_vt_tiles][Hkv][d][64]
   size_t off_o_pre, off_lse_pre, off_o_loc, off_lse_loc;  // forward
   size_t off_delta, off_dq_acc;                           // backward
   // backward, query-tile order per kv head: Q and dO rows [n_qtiles][Hkv][128][d],
