@@ -30,8 +30,8 @@
 // registers. V is transposed once per call into 64-key tiles [d][key] whose
 // keys sit in the MFMA operand-slot order, so its operand is a plain 16-byte
 // row read (the transposing LDS read runs at about half that rate). The
-// running max is only raised (and O, l rescaled) when a row's max grows by more
-// than 2^8, which keeps P <= 256 and skips almost every rescale.
+// softmax reference is each row's max over the wave's first tile and is only
+// raised when a row sum would pass 2^64, so no per-tile max is taken.
 #include <climits>
 
 #include "launch.hpp"
@@ -40,7 +40,6 @@ namespace ba {
 
 namespace {
 
-constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 template <int HD>
 struct FwdState {
@@ -49,6 +48,7 @@ struct FwdState {
   bf16x8 qf[KS];
   f32x16 acc[DT];
   float m_run, l_run;
+  bool started;  // the running max has been set (wave-uniform)
   int end, wmin, wmax;
   int lane;
   uint32_t k_base, k_t;  // K row reads
@@ -103,7 +103,38 @@ __device__ __forceinline__ void fwd_mphase(FwdState<HD> &st, const bf16 *sVt, co
 }
 
 // Softmax phase for the tile [k0, k0 + 64): mask keys past each row's prefix
-// end, raise the running max if needed, and form P^T in bf16.
+// end and form P^T = exp2(S * scale * log2(e) - m) in bf16. The reference m is
+// the row max of the wave's first tile and is not re-derived per tile: a later
+// score above it only makes P larger than 1, which bf16 and the fp32 sums hold
+// exactly in relative terms. Only when a lane's partial row sum passes 2^64 is
+// the tile's true max taken, O and l rescaled to it and P formed again.
+template <int HD>
+__device__ __forceinline__ float tile_row_max(const f32x16 (&s)[2], float sl2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+  return half_max(mx) * sl2;
+}
+
+// P^T in bf16 against the current reference; returns this lane's partial row sum.
+template <int HD>
+__device__ __forceinline__ float fwd_form_p(const FwdState<HD> &st, const f32x16 (&s)[2], float sl2,
+                                            bf16x8 (&pb)[4]) {
+  const float m_use = (st.m_run == -INFINITY) ? 0.0f : st.m_run;  // padding rows stay at -inf
+  float rs = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(fmaf(s[kb][i], sl2, -m_use));
+      rs += p;
+      pb[kb * 2 + (i >> 3)][i & 7] = (bf16)p;
+    }
+  return rs;
+}
+
 template <int HD>
 __device__ __forceinline__ void fwd_softmax(FwdState<HD> &st, f32x16 (&s)[2], int k0, float sl2, bf16x8 (&pb)[4]) {
   constexpr int DT = FwdState<HD>::DT;
@@ -117,30 +148,20 @@ __device__ __forceinline__ void fwd_softmax(FwdState<HD> &st, f32x16 (&s)[2], in
         if (key > st.end) s[kb][i] = -INFINITY;
       }
   }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-  const float mt = half_max(mx) * sl2;
-  if (__any(mt > st.m_run + kRescaleSlack)) {
-    const float m_new = fmaxf(st.m_run, mt);
-    const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(st.m_run - m_new);
+  if (!st.started) {  // the wave's first tile holds every row's first visible key
+    st.m_run = tile_row_max<HD>(s, sl2);
+    st.started = true;
+  }
+  float rs = fwd_form_p<HD>(st, s, sl2, pb);
+  if (__any(rs > 0x1p64f)) {  // rare: raise the reference to this tile's max and form P again
+    const float m_new = fmaxf(st.m_run, tile_row_max<HD>(s, sl2));
+    const float alpha = fast_exp2(st.m_run - m_new);
     st.l_run *= alpha;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
     st.m_run = m_new;
+    rs = fwd_form_p<HD>(st, s, sl2, pb);
   }
-  const float m_use = (st.m_run == -INFINITY) ? 0.0f : st.m_run;
-  float rs = 0.0f;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = fast_exp2(fmaf(s[kb][i], sl2, -m_use));
-      rs += p;
-      pb[kb * 2 + (i >> 3)][i & 7] = (bf16)p;
-    }
   st.l_run += rs;
 }
 
@@ -224,6 +245,7 @@ __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf
   st.wmax = wave_max(st.end);
   st.m_run = -INFINITY;
   st.l_run = 0.0f;
+  st.started = false;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) st.acc[dt] = f32x16{};
   st.lane = lane;

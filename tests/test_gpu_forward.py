@@ -108,6 +108,33 @@ def test_forward_edge_cases(name):
     _dense_check(EDGE[name]())
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_forward_rising_scores_force_rescale(d):
+    """Scores that rise by far more than 2^64 (in units of exp2) along each
+    sequence, so the softmax reference taken from the first key tile must be
+    raised several times. Q = 0.5 and K rows = a(pos) * 1 with a = (pos // 16) / 2:
+    every product and sum is exact in bf16 / fp32, and the oracle decides."""
+    w = _edge("r", "bf16", d, 4, 2, [600, 70], None, [5, 300, 599, 650], [7, 3, 16, 5],
+              [TTT, BLOCK, TTT, BLOCK])
+    t = make_inputs(w)
+    t["q"] = bf16_round_bits(np.full(to_f32(t["q"]).shape, 0.5, np.float32))
+    t["qb"] = bf16_round_bits(np.full(to_f32(t["qb"]).shape, 0.5, np.float32))
+    k = np.zeros(to_f32(t["k"]).shape, np.float32)
+    for s0, s1 in zip(w.cu_seqlens[:-1], w.cu_seqlens[1:]):
+        pos = np.arange(s1 - s0)
+        k[s0:s1] = ((pos // 16) / 2.0).astype(np.float32)[:, None, None]
+    t["k"] = bf16_round_bits(k)
+    grow = float(k.max()) * 0.5 * d / math.sqrt(d) / math.log(2.0)  # largest score, log2 units
+    say(f"[fwd rescale] d={d}: largest score {grow:.1f} (log2 units)")
+    assert grow > 96  # the first key tile tops out near 12 (d = 128) or 9 (d = 64)
+    _, _, (o, lse, ob, lseb) = _run_fwd(w, t)
+    ref = oracle.forward(oracle.Problem.from_workload(w), f64_all(t))
+    check_out("o", host(o), ref["o"], "bf16", "o")
+    check_out("ob", host(ob), ref["ob"], "bf16", "o")
+    check_out("lse", host(lse), ref["lse"], "bf16", "lse")
+    check_out("lseb", host(lseb), ref["lseb"], "bf16", "lse")
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["qwen3_8b_16k", "dflash_64k", "ctx256k_rank3", "gptoss_128k_mixed"])
 def test_forward_full_size_sampled_rows(name):
