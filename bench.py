@@ -205,7 +205,8 @@ def main():
     pairs = sum(plan.pairs)
     flops_fwd, flops_bwd = plan.flops_fwd(), plan.flops_bwd()
     value = (flops_fwd + flops_bwd) / (ms * 1e-3) / 1e12
-    fwd_ms = sum(kern[k][0] for k in ("metadata_upload", "main_fwd", "branch_local_fwd", "lse_merge")) / args.steps
+    fwd_kernels = ("metadata_upload", "vt_transpose", "main_fwd", "branch_local_fwd", "lse_merge")
+    fwd_ms = sum(kern[k][0] for k in fwd_kernels if k in kern) / args.steps
     bwd_ms = ms - fwd_ms
     main_pairs = plan.pairs[0] + plan.pairs[1]
     # contraction flops each kernel must do per visible (row, key) pair and q head:
