@@ -181,7 +181,7 @@ __device__ __forceinline__ void stage_rows(bf16 *lds, const bf16 *__restrict__ s
 // (16 bytes per lane, gfx950): each wave's 1 KB block of the swizzled tile is
 // written straight into LDS, lane l of block b fetching the logical chunk that
 // the swizzle places at LDS offset b*1KB + 16*l. Completion is tracked by
-// vmcnt: wait_async_loads() then a barrier before the tile is read.
+// vmcnt: dma_barrier() before the tile is read.
 //
 // The per-lane part of each address (row within the tile, chunk) is fixed for
 // the kernel's life, so it is computed once; a tile only moves the uniform base.
@@ -250,7 +250,24 @@ __device__ __forceinline__ void stage_words_async(void *lds, const void *__restr
                                      4, 0, 0);
 }
 
-__device__ __forceinline__ void wait_async_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Workgroup barrier after this wave's LDS reads and all but its VM most recent
+// vector-memory requests (LDS DMA among them) have completed: every tile
+// requested before those is in LDS for every wave after the barrier, and no
+// LDS read of the phase before it is still in flight. The wait goes through the
+// builtin so the compiler's own wait insertion sees it: with a wait it cannot
+// see, it assumes a DMA into a buffer may still be pending when the buffer is
+// next read and waits for every load in flight, including DMA just issued for
+// later tiles. The empty asm statements stop the compiler moving memory
+// accesses across. VM = 63 waits for LDS reads only.
+template <int VM>
+__device__ __forceinline__ void dma_barrier() {
+  static_assert(VM >= 0 && VM <= 63, "vmcnt field");
+  asm volatile("" ::: "memory");
+  // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | 0x0070);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ bf16x8 join(i16x4 a, i16x4 b) {
   typedef short i16x8 __attribute__((ext_vector_type(8)));

@@ -161,16 +161,14 @@ __global__ __launch_bounds__(256, 2) void main_bwd_dq_bf16_kernel(Meta mt, const
 
   for (int j = 0; j < ntiles; j += 2) {
     const int k0 = kv_lo + j * BN;
-    wait_async_loads();
-    __syncthreads();  // tile j is in buffer 0; every wave is done with buffer 1
+    dma_barrier<0>();  // tile j is in buffer 0; every wave is done with buffer 1
     if (j + 1 < ntiles) {
       kvt.load(sK1, kg, k0 + BN, kv_end);
       kvt.load(sV1, vg, k0 + BN, kv_end);
     }
     if (k0 <= wmax) dq_tile<HD>(st, sK0, sV0, k0, sl2);
     if (j + 1 >= ntiles) break;
-    wait_async_loads();
-    __syncthreads();  // tile j+1 is in buffer 1; every wave is done with buffer 0
+    dma_barrier<0>();  // tile j+1 is in buffer 1; every wave is done with buffer 0
     if (j + 2 < ntiles) {
       kvt.load(sK0, kg, k0 + 2 * BN, kv_end);
       kvt.load(sV0, vg, k0 + 2 * BN, kv_end);
@@ -287,7 +285,9 @@ struct DkdvState {
   f32x16 adk[KB][DT], adv[KB][DT];
   int my_key[KB];
   int wkey_lo, key_hi;
-  int grp, in_j, in_q, lane;
+  int lane;
+  uint32_t r_base, r_t;        // row reads of Q, dO (A operands of S, dP)
+  uint32_t t_base[2], t_t[2];  // transposing reads of dO, Q (B operands of dV, dK), c = 0, 1
 };
 
 // Rows of one staged query tile against the wave's 32*KB keys; MASK when some
@@ -303,7 +303,17 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
     // Rows 32rb..32rb+31: S first, turned into P (kept as the bf16 operand of
     // dV, which also serves dS), then dP, so only one score block is live.
     // element i: row rb*32 + (i/4)*8 + 4*(lane/32) + i%4, key my_key[b]
-    const int ar = rb * 32 + (lane & 31);
+    // LDS addresses come from two per-lane terms per pattern (one xad per read);
+    // precomputed per read they would cost ~30 registers and push the kernel
+    // into spills, whose reloads share the in-order counter with the DMA.
+    opaque(st.r_base);
+    opaque(st.r_t);
+    opaque(st.t_base[0]);
+    opaque(st.t_base[1]);
+    opaque(st.t_t[0]);
+    opaque(st.t_t[1]);
+    const uint32_t rb_ = st.r_base, rt_ = st.r_t, tb0 = st.t_base[0], tb1 = st.t_base[1], tt0 = st.t_t[0],
+                   tt1 = st.t_t[1];
     bf16x8 pa[KB][2], dsa[KB][2];
     {
       f32x16 sc[KB];
@@ -311,7 +321,7 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
       for (int b = 0; b < KB; ++b) sc[b] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(sQ + ar * HD + (((2 * ks + (lane >> 5)) ^ swz<HD>(ar)) << 3));
+        const bf16x8 aq = row_read<HD>(sQ, rb_, rt_, rb, ks);
 #pragma unroll
         for (int b = 0; b < KB; ++b) sc[b] = mfma32(aq, st.kf[b][ks], sc[b]);
       }
@@ -339,7 +349,7 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
       for (int b = 0; b < KB; ++b) dp[b] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ao = *reinterpret_cast<const bf16x8 *>(sdO + ar * HD + (((2 * ks + (lane >> 5)) ^ swz<HD>(ar)) << 3));
+        const bf16x8 ao = row_read<HD>(sdO, rb_, rt_, rb, ks);
 #pragma unroll
         for (int b = 0; b < KB; ++b) dp[b] = mfma32(ao, st.vf[b][ks], dp[b]);
       }
@@ -360,12 +370,11 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
     // Operand slot 8*half + 4c + j <-> row 32rb + 16kh + 8c + 4*half + j.
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      const int row0 = rb * 32 + kh * 16 + 4 * (st.grp >> 1) + st.in_j;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int d = dt * 32 + (st.grp & 1) * 16 + 4 * st.in_q;
-        const bf16x8 bo = join(lds_read_tr(sdO + lds_off<HD>(row0, d)), lds_read_tr(sdO + lds_off<HD>(row0 + 8, d)));
-        const bf16x8 bq = join(lds_read_tr(sQ + lds_off<HD>(row0, d)), lds_read_tr(sQ + lds_off<HD>(row0 + 8, d)));
+        const int kk = 2 * rb + kh;
+        const bf16x8 bo = join(tr_read<HD>(sdO, tb0, tt0, kk, dt), tr_read<HD>(sdO, tb1, tt1, kk, dt));
+        const bf16x8 bq = join(tr_read<HD>(sQ, tb0, tt0, kk, dt), tr_read<HD>(sQ, tb1, tt1, kk, dt));
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
           st.adv[b][dt] = mfma32(pa[b][kh], bo, st.adv[b][dt]);
@@ -457,18 +466,16 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void main_bwd_dkdv_bf16_kernel(Met
     }
   }
   st.lane = lane;
-  st.grp = lane >> 4;
-  st.in_j = (lane & 15) >> 2;
-  st.in_q = lane & 3;
+  row_read_init<HD>(lane & 31, lane, st.r_base, st.r_t);
+  tr_read_init<HD>(lane, 0, st.t_base[0], st.t_t[0]);
+  tr_read_init<HD>(lane, 1, st.t_base[1], st.t_t[1]);
 
   for (int qi = kt.qt_begin; qi < kt.qt_end; qi += 2) {
-    wait_async_loads();
-    __syncthreads();  // tile qi is in buffer 0; every wave is done with buffer 1
+    dma_barrier<0>();  // tile qi is in buffer 0; every wave is done with buffer 1
     if (qi + 1 < kt.qt_end) prefetch(qi + 1, sQ1, sO1, sL1, sD1, sE1);
     dkdv_tile<HD, KB>(st, sQ0, sO0, sL0, sD0, sE0, sl2);
     if (qi + 1 >= kt.qt_end) break;
-    wait_async_loads();
-    __syncthreads();  // tile qi+1 is in buffer 1; every wave is done with buffer 0
+    dma_barrier<0>();  // tile qi+1 is in buffer 1; every wave is done with buffer 0
     if (qi + 2 < kt.qt_end) prefetch(qi + 2, sQ0, sO0, sL0, sD0, sE0);
     dkdv_tile<HD, KB>(st, sQ1, sO1, sL1, sD1, sE1, sl2);
   }

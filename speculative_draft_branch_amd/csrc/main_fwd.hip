@@ -165,25 +165,6 @@ __device__ __forceinline__ void fwd_softmax(FwdState<HD> &st, f32x16 (&s)[2], in
   st.l_run += rs;
 }
 
-// Workgroup barrier between phases. The LDS reads of the phase are complete
-// before it (their buffers may be refilled right after); with WAIT_DMA the
-// wave's outstanding LDS DMA is complete too, so after the barrier every
-// requested tile is in LDS. The waits go through the builtin so the compiler's
-// own wait insertion knows about them: otherwise it assumes the DMA into a
-// buffer is still pending when that buffer is next read and waits for every
-// load in flight, including the ones just issued for later tiles. The empty
-// asm statements keep the compiler from moving memory accesses across.
-template <bool WAIT_DMA>
-__device__ __forceinline__ void phase_barrier() {
-  asm volatile("" ::: "memory");
-  // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
-  if constexpr (WAIT_DMA)
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-  else
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 }  // namespace
 
@@ -263,7 +244,7 @@ __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf
   const bf16 *vtg = vt + ((int64_t)mt.vt_base[tile_a.seq] * hkv + g) * (HD * 64);
   const int64_t vt_stride = (int64_t)hkv * HD * 64;  // between consecutive V^T tiles
   kt.load(sK0, kg, kv_lo, kv_end);
-  phase_barrier<true>();
+  dma_barrier<0>();
 
   // Phase slots: slot t runs, for group grpi, local phase u = t - grpi; even u
   // is the matrix phase of tile j = u/2 (P V of tile j-1, S of tile j), odd u
@@ -299,8 +280,8 @@ __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf
           const int js = jj - 1 + h2;
           if (js >= 0 && js < ntiles && kv_lo + js * BN <= st.wmax) fwd_softmax<HD>(st, s, kv_lo + js * BN, sl2, pb);
         }
-        if (h2 == 0) phase_barrier<false>();
-        else phase_barrier<true>();
+        if (h2 == 0) dma_barrier<63>();
+        else dma_barrier<0>();
       }
     }
   }
