@@ -157,6 +157,13 @@ __device__ __forceinline__ i16x4 tr_read(const bf16 *tile, uint32_t base, uint32
 // addresses derived from it are recomputed where they are used (one VALU op per
 // read) rather than hoisted into one live register per read.
 __device__ __forceinline__ void opaque(uint32_t &x) { asm volatile("" : "+v"(x)); }
+// The lane id, recomputed where it is used (two VALU ops) instead of living in
+// a register across a loop; the compiler cannot hoist or spill it.
+__device__ __forceinline__ int lane_id_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
 
 // Stage rows [k0, k0 + ROWS) of a [rows, Hkv, HD] bf16 tensor (kv head g) into
 // an LDS tile in the swizzled layout; rows past `last` (inclusive bound) are

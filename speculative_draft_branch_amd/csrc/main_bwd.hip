@@ -297,9 +297,9 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
                                           const float *sD, const int *sEnd, float sl2) {
   constexpr int BM = kTileRows;
   constexpr int KS = DkdvState<HD, KB>::KS, DT = DkdvState<HD, KB>::DT;
-  const int lane = st.lane;
 #pragma unroll 1
   for (int rb = 0; rb < BM / 32; ++rb) {
+    const int lane = lane_id_here();
     // Rows 32rb..32rb+31: S first, turned into P (kept as the bf16 operand of
     // dV, which also serves dS), then dP, so only one score block is live.
     // element i: row rb*32 + (i/4)*8 + 4*(lane/32) + i%4, key my_key[b]
