@@ -414,10 +414,13 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void main_bwd_dkdv_bf16_kernel(Met
   constexpr int KB = kDkdvBlocks, NT = kDkdvThreads;
   constexpr int KS = HD / 16, DT = HD / 32;
   static_assert(kBwdKeys == 32 * KB * (NT / 64) && BM == 128, "tile shape");
-  __shared__ __attribute__((aligned(16))) bf16 sQ0[BM * HD];
-  __shared__ __attribute__((aligned(16))) bf16 sO0[BM * HD];
-  __shared__ __attribute__((aligned(16))) bf16 sQ1[BM * HD];
-  __shared__ __attribute__((aligned(16))) bf16 sO1[BM * HD];
+  // Q and dO of one buffer share an array, so a read of either is one address
+  // plus a constant offset; the two buffers stay distinct objects, which lets
+  // the compiler see that reads of one never wait for DMA into the other.
+  __shared__ __attribute__((aligned(16))) bf16 sQO0[2 * BM * HD];
+  __shared__ __attribute__((aligned(16))) bf16 sQO1[2 * BM * HD];
+  bf16 *const sQ0 = sQO0, *const sO0 = sQO0 + BM * HD;
+  bf16 *const sQ1 = sQO1, *const sO1 = sQO1 + BM * HD;
   __shared__ __attribute__((aligned(16))) float sL0[BM], sD0[BM], sL1[BM], sD1[BM];
   __shared__ __attribute__((aligned(16))) int sE0[kTileMetaWords], sE1[kTileMetaWords];
 
