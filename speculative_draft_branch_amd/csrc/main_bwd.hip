@@ -41,11 +41,12 @@ struct DqState {
 };
 
 // One 64-key tile [k0, k0 + 64) of the wave's 32 rows against LDS tiles sK, sV.
-template <int HD>
+// MASK: some key of the tile lies past some row's prefix end (a wave-uniform
+// condition, so the unmasked tiles carry no per-element selects).
+template <int HD, bool MASK>
 __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const bf16 *sV, int k0, float sl2) {
   constexpr int KS = DqState<HD>::KS, DT = DqState<HD>::DT;
   const int lane = st.lane;
-  const bool need_mask = k0 + 63 > st.wmin;
   // One 32-key block at a time: S^T, dP^T, dS^T, then its two dQ k-steps.
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -61,7 +62,7 @@ __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const b
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float p = fast_exp2(fmaf(s[i], sl2, -st.l2));
-      if (need_mask) {
+      if constexpr (MASK) {
         const int key = k0 + kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
         if (key > st.end) p = 0.0f;
       }
@@ -97,10 +98,12 @@ __global__ __launch_bounds__(256, 2) void main_bwd_dq_bf16_kernel(Meta mt, const
                                                                float *__restrict__ dq_acc) {
   constexpr int BN = 64;
   constexpr int KS = HD / 16, DT = HD / 32;
-  __shared__ __attribute__((aligned(16))) bf16 sK0[BN * HD];
-  __shared__ __attribute__((aligned(16))) bf16 sV0[BN * HD];
-  __shared__ __attribute__((aligned(16))) bf16 sK1[BN * HD];
-  __shared__ __attribute__((aligned(16))) bf16 sV1[BN * HD];
+  // K and V of one buffer share an array (one address for both reads); the
+  // two buffers stay distinct objects for the compiler's DMA wait tracking.
+  __shared__ __attribute__((aligned(16))) bf16 sKV0[2 * BN * HD];
+  __shared__ __attribute__((aligned(16))) bf16 sKV1[2 * BN * HD];
+  bf16 *const sK0 = sKV0, *const sV0 = sKV0 + BN * HD;
+  bf16 *const sK1 = sKV1, *const sV1 = sKV1 + BN * HD;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hkv = mt.hkv, G = mt.G;
@@ -166,14 +169,20 @@ __global__ __launch_bounds__(256, 2) void main_bwd_dq_bf16_kernel(Meta mt, const
       kvt.load(sK1, kg, k0 + BN, kv_end);
       kvt.load(sV1, vg, k0 + BN, kv_end);
     }
-    if (k0 <= wmax) dq_tile<HD>(st, sK0, sV0, k0, sl2);
+    if (k0 <= wmax) {
+      if (k0 + 63 > st.wmin) dq_tile<HD, true>(st, sK0, sV0, k0, sl2);
+      else dq_tile<HD, false>(st, sK0, sV0, k0, sl2);
+    }
     if (j + 1 >= ntiles) break;
     dma_barrier<0>();  // tile j+1 is in buffer 1; every wave is done with buffer 0
     if (j + 2 < ntiles) {
       kvt.load(sK0, kg, k0 + 2 * BN, kv_end);
       kvt.load(sV0, vg, k0 + 2 * BN, kv_end);
     }
-    if (k0 + BN <= wmax) dq_tile<HD>(st, sK1, sV1, k0 + BN, sl2);
+    if (k0 + BN <= wmax) {
+      if (k0 + BN + 63 > st.wmin) dq_tile<HD, true>(st, sK1, sV1, k0 + BN, sl2);
+      else dq_tile<HD, false>(st, sK1, sV1, k0 + BN, sl2);
+    }
   }
   if (row >= 0) {
     float *dst = dq_acc + ((int64_t)row * mt.hq + h) * HD;
