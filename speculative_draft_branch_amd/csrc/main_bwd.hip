@@ -41,6 +41,8 @@ struct DqState {
 };
 
 // One 64-key tile [k0, k0 + 64) of the wave's 32 rows against LDS tiles sK, sV.
+constexpr int kDqRing = 4;
+
 // MASK: some key of the tile lies past some row's prefix end (a wave-uniform
 // condition, so the unmasked tiles carry no per-element selects).
 template <int HD, bool MASK>
@@ -52,11 +54,24 @@ __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const b
   for (int kb = 0; kb < 2; ++kb) {
     f32x16 s = f32x16{}, dp = f32x16{};
     const int r = kb * 32 + (lane & 31);
+    // S^T and dP^T as one software pipeline of (LDS read, MFMA) steps, step
+    // 2ks reading K and 2ks+1 reading V, with kDqRing operands in flight; the
+    // scheduling barriers keep the compiler from sinking each read next to its
+    // MFMA and waiting for it there.
+    auto rd = [&](int i) {
+      const int off = r * HD + (((2 * (i >> 1) + (lane >> 5)) ^ swz<HD>(r)) << 3);
+      return *reinterpret_cast<const bf16x8 *>(((i & 1) ? sV : sK) + off);
+    };
+    bf16x8 ring[kDqRing];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int off = r * HD + (((2 * ks + (lane >> 5)) ^ swz<HD>(r)) << 3);
-      s = mfma32(*reinterpret_cast<const bf16x8 *>(sK + off), st.qf[ks], s);
-      dp = mfma32(*reinterpret_cast<const bf16x8 *>(sV + off), st.of[ks], dp);
+    for (int i = 0; i < kDqRing; ++i) ring[i] = rd(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      if (i & 1) dp = mfma32(ring[i % kDqRing], st.of[i >> 1], dp);
+      else s = mfma32(ring[i % kDqRing], st.qf[i >> 1], s);
+      if (i + kDqRing < 2 * KS) ring[i % kDqRing] = rd(i + kDqRing);
+      __builtin_amdgcn_sched_barrier(0);
     }
     bf16x8 db[2];  // dS^T operands of the block's two 16-key k-steps
 #pragma unroll
