@@ -324,9 +324,8 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
 #pragma unroll 1
   for (int rb = 0; rb < BM / 32; ++rb) {
     const int lane = lane_id_here();
-    // Rows 32rb..32rb+31: S first, turned into P (kept as the bf16 operand of
-    // dV, which also serves dS), then dP, so only one score block is live.
-    // element i: row rb*32 + (i/4)*8 + 4*(lane/32) + i%4, key my_key[b]
+    // Rows 32rb..32rb+31. element i: row rb*32 + (i/4)*8 + 4*(lane/32) + i%4,
+    // key my_key[b].
     // LDS addresses come from two per-lane terms per pattern (one xad per read);
     // precomputed per read they would cost ~30 registers and push the kernel
     // into spills, whose reloads share the in-order counter with the DMA.
@@ -340,19 +339,29 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
                    tt1 = st.t_t[1];
     bf16x8 pa[KB][2], dsa[KB][2];
     {
-      f32x16 sc[KB];
+      // S and dP of these rows, then P and dS element by element from the fp32
+      // values (P rounded to bf16 once, for the dV product).
+      f32x16 sc[KB], dp[KB];
 #pragma unroll
-      for (int b = 0; b < KB; ++b) sc[b] = f32x16{};
+      for (int b = 0; b < KB; ++b) {
+        sc[b] = f32x16{};
+        dp[b] = f32x16{};
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 aq = row_read<HD>(sQ, rb_, rt_, rb, ks);
+        const bf16x8 ao = row_read<HD>(sdO, rb_, rt_, rb, ks);
 #pragma unroll
-        for (int b = 0; b < KB; ++b) sc[b] = mfma32(aq, st.kf[b][ks], sc[b]);
+        for (int b = 0; b < KB; ++b) {
+          sc[b] = mfma32(aq, st.kf[b][ks], sc[b]);
+          dp[b] = mfma32(ao, st.vf[b][ks], dp[b]);
+        }
       }
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int r0 = rb * 32 + i4 * 8 + 4 * (lane >> 5);
         const f32x4 l2 = *reinterpret_cast<const f32x4 *>(sL2 + r0);
+        const f32x4 dd = *reinterpret_cast<const f32x4 *>(sD + r0);
         int4 ends = {0, 0, 0, 0};
         if constexpr (MASK) ends = *reinterpret_cast<const int4 *>(sEnd + r0);
 #pragma unroll
@@ -363,30 +372,8 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
             float p = fast_exp2(fmaf(sc[b][i], sl2, -l2[e]));
             if (MASK && (ends[e] < st.my_key[b] || st.my_key[b] >= st.key_hi)) p = 0.0f;
             pa[b][i >> 3][i & 7] = (bf16)p;
+            dsa[b][i >> 3][i & 7] = (bf16)(p * (dp[b][i] - dd[e]));
           }
-        }
-      }
-    }
-    {
-      f32x16 dp[KB];
-#pragma unroll
-      for (int b = 0; b < KB; ++b) dp[b] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ao = row_read<HD>(sdO, rb_, rt_, rb, ks);
-#pragma unroll
-        for (int b = 0; b < KB; ++b) dp[b] = mfma32(ao, st.vf[b][ks], dp[b]);
-      }
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int r0 = rb * 32 + i4 * 8 + 4 * (lane >> 5);
-        const f32x4 dd = *reinterpret_cast<const f32x4 *>(sD + r0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = i4 * 4 + e;
-#pragma unroll
-          for (int b = 0; b < KB; ++b)
-            dsa[b][i >> 3][i & 7] = (bf16)((float)pa[b][i >> 3][i & 7] * (dp[b][i] - dd[e]));
         }
       }
     }
