@@ -112,6 +112,59 @@ __device__ __forceinline__ int lds_off(int row, int d) {  // element offset of (
   return row * HD + ((((d >> 3) ^ swz<HD>(row))) << 3) + (d & 7);
 }
 
+// Padded LDS tiles: each row of HD bf16 followed by 48 unused bytes (19 four-
+// bank groups per row at d = 128, an odd count). Sixteen consecutive rows at
+// the same column then start in sixteen different 4-bank groups, so operand
+// reads need no swizzle and every operand's address is a per-lane base plus a
+// constant (no address arithmetic per read). Measured against 16 and 32 bytes
+// of padding, 48 gave the fewest bank conflicts over the two read patterns. A
+// row is written by one LDS DMA instruction, 4 bytes per lane (HD / 2 lanes).
+template <int HD>
+constexpr int kPadRowBytes = HD * 2 + 48;
+
+// Rows [0, ROWS) of a contiguous [rows][HD] bf16 source into a padded LDS tile;
+// rows r with r % NW == w are this wave's. Asynchronous (vmcnt).
+template <int HD, int ROWS, int NW>
+__device__ __forceinline__ void stage_padded_async(bf16 *lds, const bf16 *__restrict__ src, int wave, int lane) {
+  static_assert(ROWS % NW == 0, "rows per wave");
+  constexpr int LANES = HD / 2;  // 4-byte lanes per row
+  const int w = uni(wave);  // row choice, hence both addresses' row parts, is wave-uniform
+  const uint32_t lane_off = (uint32_t)lane * 4u;
+#pragma unroll
+  for (int it = 0; it < ROWS / NW; ++it) {
+    const int r = it * NW + w;
+    const char *row = reinterpret_cast<const char *>(src + (int64_t)r * HD);
+    if (LANES == 64 || lane < LANES)
+      __builtin_amdgcn_global_load_lds(row + lane_off,
+                                       (__attribute__((address_space(3))) void *)(reinterpret_cast<char *>(lds) +
+                                                                                  r * kPadRowBytes<HD>),
+                                       4, 0, 0);
+  }
+}
+// Row read (A operand with k = column): lane reads row 32*blk + lane%32,
+// columns 16*ks + 8*(lane/32) .. +7.
+template <int HD>
+__device__ __forceinline__ uint32_t pad_row_base(int lane) {
+  return (uint32_t)((lane & 31) * kPadRowBytes<HD> + (lane >> 5) * 16);
+}
+template <int HD>
+__device__ __forceinline__ bf16x8 pad_row_read(const bf16 *tile, uint32_t base, int blk, int ks) {
+  return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(tile) + base +
+                                           blk * 32 * kPadRowBytes<HD> + ks * 32);
+}
+// Transposing read (operand with k = row): the 16-lane group g = lane/16 reads
+// rows 16*kk + 4*(g/2) + (lane%16)/4 + 8c, columns 32*dt + 16*(g%2) + 4*(lane%4) .. +3.
+template <int HD>
+__device__ __forceinline__ uint32_t pad_tr_base(int lane) {
+  const int g = lane >> 4, in_j = (lane & 15) >> 2, in_q = lane & 3;
+  return (uint32_t)((4 * (g >> 1) + in_j) * kPadRowBytes<HD> + (16 * (g & 1) + 4 * in_q) * 2);
+}
+template <int HD>
+__device__ __forceinline__ i16x4 pad_tr_read(const bf16 *tile, uint32_t base, int c, int kk, int dt) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(
+      reinterpret_cast<const char *>(tile) + base + (16 * kk + 8 * c) * kPadRowBytes<HD> + dt * 64));
+}
+
 // Per-lane addressing of MFMA operand reads from a swizzled [row][HD] bf16 LDS
 // tile. The swizzle XORs chunk-index bits that the k-step (or d-block) index
 // and the lane's own chunk bits never share, so an operand's byte offset is

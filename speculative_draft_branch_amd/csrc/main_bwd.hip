@@ -310,8 +310,8 @@ struct DkdvState {
   int my_key[KB];
   int wkey_lo, key_hi;
   int lane;
-  uint32_t r_base, r_t;        // row reads of Q, dO (A operands of S, dP)
-  uint32_t t_base[2], t_t[2];  // transposing reads of dO, Q (B operands of dV, dK), c = 0, 1
+  uint32_t r_base;  // padded-tile row reads of Q, dO (A operands of S, dP)
+  uint32_t t_base;  // padded-tile transposing reads of dO, Q (B operands of dV, dK)
 };
 
 // Rows of one staged query tile against the wave's 32*KB keys; MASK when some
@@ -326,17 +326,6 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
     const int lane = lane_id_here();
     // Rows 32rb..32rb+31. element i: row rb*32 + (i/4)*8 + 4*(lane/32) + i%4,
     // key my_key[b].
-    // LDS addresses come from two per-lane terms per pattern (one xad per read);
-    // precomputed per read they would cost ~30 registers and push the kernel
-    // into spills, whose reloads share the in-order counter with the DMA.
-    opaque(st.r_base);
-    opaque(st.r_t);
-    opaque(st.t_base[0]);
-    opaque(st.t_base[1]);
-    opaque(st.t_t[0]);
-    opaque(st.t_t[1]);
-    const uint32_t rb_ = st.r_base, rt_ = st.r_t, tb0 = st.t_base[0], tb1 = st.t_base[1], tt0 = st.t_t[0],
-                   tt1 = st.t_t[1];
     bf16x8 pa[KB][2], dsa[KB][2];
     {
       // S and dP of these rows, then P and dS element by element from the fp32
@@ -349,8 +338,8 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 aq = row_read<HD>(sQ, rb_, rt_, rb, ks);
-        const bf16x8 ao = row_read<HD>(sdO, rb_, rt_, rb, ks);
+        const bf16x8 aq = pad_row_read<HD>(sQ, st.r_base, rb, ks);
+        const bf16x8 ao = pad_row_read<HD>(sdO, st.r_base, rb, ks);
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
           sc[b] = mfma32(aq, st.kf[b][ks], sc[b]);
@@ -384,8 +373,8 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int kk = 2 * rb + kh;
-        const bf16x8 bo = join(tr_read<HD>(sdO, tb0, tt0, kk, dt), tr_read<HD>(sdO, tb1, tt1, kk, dt));
-        const bf16x8 bq = join(tr_read<HD>(sQ, tb0, tt0, kk, dt), tr_read<HD>(sQ, tb1, tt1, kk, dt));
+        const bf16x8 bo = join(pad_tr_read<HD>(sdO, st.t_base, 0, kk, dt), pad_tr_read<HD>(sdO, st.t_base, 1, kk, dt));
+        const bf16x8 bq = join(pad_tr_read<HD>(sQ, st.t_base, 0, kk, dt), pad_tr_read<HD>(sQ, st.t_base, 1, kk, dt));
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
           st.adv[b][dt] = mfma32(pa[b][kh], bo, st.adv[b][dt]);
@@ -425,13 +414,15 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void main_bwd_dkdv_bf16_kernel(Met
   constexpr int KB = kDkdvBlocks, NT = kDkdvThreads;
   constexpr int KS = HD / 16, DT = HD / 32;
   static_assert(kBwdKeys == 32 * KB * (NT / 64) && BM == 128, "tile shape");
-  // Q and dO of one buffer share an array, so a read of either is one address
-  // plus a constant offset; the two buffers stay distinct objects, which lets
-  // the compiler see that reads of one never wait for DMA into the other.
-  __shared__ __attribute__((aligned(16))) bf16 sQO0[2 * BM * HD];
-  __shared__ __attribute__((aligned(16))) bf16 sQO1[2 * BM * HD];
-  bf16 *const sQ0 = sQO0, *const sO0 = sQO0 + BM * HD;
-  bf16 *const sQ1 = sQO1, *const sO1 = sQO1 + BM * HD;
+  // Padded tiles (see stage_padded_async). Q and dO of one buffer share an
+  // array, so a read of either is one address plus a constant offset; the two
+  // buffers stay distinct objects, which lets the compiler see that reads of
+  // one never wait for DMA into the other.
+  constexpr int TILE = BM * kPadRowBytes<HD> / 2;  // elements per padded tile
+  __shared__ __attribute__((aligned(16))) bf16 sQO0[2 * TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sQO1[2 * TILE];
+  bf16 *const sQ0 = sQO0, *const sO0 = sQO0 + TILE;
+  bf16 *const sQ1 = sQO1, *const sO1 = sQO1 + TILE;
   __shared__ __attribute__((aligned(16))) float sL0[BM], sD0[BM], sL1[BM], sD1[BM];
   __shared__ __attribute__((aligned(16))) int sE0[kTileMetaWords], sE1[kTileMetaWords];
 
@@ -442,12 +433,10 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void main_bwd_dkdv_bf16_kernel(Met
   const float sl2 = mt.scale * kLog2e;
 
   // Query tile qi, kv head g -> one LDS buffer (all asynchronous).
-  AsyncTile<HD, BM, NT> rowt;
-  rowt.init(HD, tid);
   auto prefetch = [&](int qi, bf16 *sQ, bf16 *sO, float *sL, float *sD, int *sE) {
     const int64_t tb = ((int64_t)qi * hkv + g) * BM;
-    rowt.load(sQ, qt_rows + tb * HD, 0, BM - 1);
-    rowt.load(sO, do_rows + tb * HD, 0, BM - 1);
+    stage_padded_async<HD, BM, NT / 64>(sQ, qt_rows + tb * HD, wave, lane);
+    stage_padded_async<HD, BM, NT / 64>(sO, do_rows + tb * HD, wave, lane);
     if (wave == 0) stage_words_async<BM / 64>(sL, lt + tb, lane);
     else if (wave == 1) stage_words_async<BM / 64>(sD, dtt + tb, lane);
     else if (wave == 2) stage_words_async<kTileMetaWords / 64>(sE, et + (int64_t)qi * kTileMetaWords, lane);
@@ -480,9 +469,8 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void main_bwd_dkdv_bf16_kernel(Met
     }
   }
   st.lane = lane;
-  row_read_init<HD>(lane & 31, lane, st.r_base, st.r_t);
-  tr_read_init<HD>(lane, 0, st.t_base[0], st.t_t[0]);
-  tr_read_init<HD>(lane, 1, st.t_base[1], st.t_t[1]);
+  st.r_base = pad_row_base<HD>(lane);
+  st.t_base = pad_tr_base<HD>(lane);
 
   for (int qi = kt.qt_begin; qi < kt.qt_end; qi += 2) {
     dma_barrier<0>();  // tile qi is in buffer 0; every wave is done with buffer 1
