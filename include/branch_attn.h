@@ -118,7 +118,8 @@ ba_status_t ba_plan_pairs(const ba_plan_t *plan, int64_t out[3]);
 /* Forward pass: o/lse for main rows, ob/lseb for branch rows (merged result).
  * Enqueues: metadata upload into the workspace, the main-sequence kernel (all
  * rows against their causal main prefix), the branch-local kernel and the
- * log-sum-exp merge. workspace: device buffer of ws_bytes >= ba_workspace_bytes(plan, 0). */
+ * log-sum-exp merge; for BA_BF16 the merge runs inside the branch-local kernel
+ * (no float32 branch-local partial in HBM). workspace: device buffer of ws_bytes >= ba_workspace_bytes(plan, 0). */
 ba_status_t branch_attn_fwd(const ba_plan_t *plan,
                             const void *q, const void *k, const void *v,
                             const void *qb, const void *kb, const void *vb,

@@ -115,6 +115,7 @@ Meta make_meta(const ba_plan *pl, const void *ws) {
   m.n_ktiles = pl->n_ktiles;
   m.n_fwd_pairs = pl->n_fwd_pairs;
   m.n_vt_tiles = pl->n_vt_tiles;
+  m.max_branch = pl->max_branch;
   m.scale = pl->scale;
   return m;
 }
@@ -221,8 +222,12 @@ ba_status_t ba_branch_local_fwd(const ba_plan_t *pl, const void *qb, const void 
   BA_TRY(check_ws(pl, workspace, ws_bytes, 2));
   hipStream_t st = static_cast<hipStream_t>(stream);
   BA_TRY(upload(pl, workspace, st));
+  const Meta mt = make_meta(pl, workspace);
   BA_TRY(timed(K_BRANCH_LOCAL_FWD, st, "branch-local forward", [&] {
-    return launch_branch_local_fwd(make_meta(pl, workspace), pl->dtype, qb, kb, vb, o_loc, lse_loc, st);
+    if (pl->dtype == BA_BF16)
+      return launch_branch_fwd_bf16(mt, (const bf16 *)qb, (const bf16 *)kb, (const bf16 *)vb, nullptr, nullptr, o_loc,
+                                    lse_loc, nullptr, nullptr, st);
+    return launch_branch_local_fwd(mt, pl->dtype, qb, kb, vb, o_loc, lse_loc, st);
   }));
   return BA_OK;
 }
@@ -267,9 +272,14 @@ ba_status_t branch_attn_fwd(const ba_plan_t *pl, const void *q, const void *k, c
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   float *o_pre = reinterpret_cast<float *>(ws + pl->off_o_pre);
   float *lse_pre = reinterpret_cast<float *>(ws + pl->off_lse_pre);
+  BA_TRY(run_main_fwd(pl, mt, q, qb, k, v, o, lse, o_pre, lse_pre, workspace, st));
+  if (pl->dtype == BA_BF16)  // branch-local attention and the merge in one kernel
+    return timed(K_BRANCH_LOCAL_FWD, st, "branch-local forward + merge", [&] {
+      return launch_branch_fwd_bf16(mt, (const bf16 *)qb, (const bf16 *)kb, (const bf16 *)vb, o_pre, lse_pre, nullptr,
+                                    nullptr, (bf16 *)ob, lseb, st);
+    });
   float *o_loc = reinterpret_cast<float *>(ws + pl->off_o_loc);
   float *lse_loc = reinterpret_cast<float *>(ws + pl->off_lse_loc);
-  BA_TRY(run_main_fwd(pl, mt, q, qb, k, v, o, lse, o_pre, lse_pre, workspace, st));
   BA_TRY(timed(K_BRANCH_LOCAL_FWD, st, "branch-local forward",
                [&] { return launch_branch_local_fwd(mt, pl->dtype, qb, kb, vb, o_loc, lse_loc, st); }));
   BA_TRY(timed(K_LSE_MERGE, st, "lse_merge", [&] {
@@ -335,6 +345,14 @@ ba_status_t branch_attn_bwd(const ba_plan_t *pl, const void *q, const void *k, c
                                  (const float *)d_o, (const float *)d_ob, lse, lseb, delta, dq_acc, (float *)dk,
                                  (float *)dv, st);
     }));
+  }
+  if (pl->dtype == BA_BF16) {  // the branch kernel writes dqb itself
+    BA_TRY(timed(K_BRANCH_LOCAL_BWD, st, "branch-local backward", [&] {
+      return launch_branch_bwd_bf16(mt, (const bf16 *)qb, (const bf16 *)kb, (const bf16 *)vb, (const bf16 *)d_ob, lseb,
+                                    delta, dq_acc, (bf16 *)dqb, (bf16 *)dkb, (bf16 *)dvb, st);
+    }));
+    return timed(K_DQ_CONVERT, st, "dq convert",
+                 [&] { return launch_convert_rows(dq_acc, pl->Nq * hd, dq, pl->dtype, st); });
   }
   BA_TRY(timed(K_BRANCH_LOCAL_BWD, st, "branch-local backward", [&] {
     return launch_branch_local_bwd(mt, pl->dtype, qb, kb, vb, d_ob, lseb, delta, dq_acc, dkb, dvb, st);

@@ -38,6 +38,7 @@ struct Meta {
   int64_t N, Nq, Rb, A;
   int32_t hq, hkv, G, d, rows_per_tile;
   int32_t n_qtiles, n_ktiles, n_fwd_pairs, n_vt_tiles;
+  int32_t max_branch;  // longest branch (rows of one anchor)
   float scale;
 };
 

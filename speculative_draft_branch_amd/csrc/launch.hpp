@@ -15,6 +15,16 @@ hipError_t launch_branch_local_fwd(const Meta &mt, ba_dtype_t dt, const void *qb
 hipError_t launch_branch_local_bwd(const Meta &mt, ba_dtype_t dt, const void *qb, const void *kb, const void *vb,
                                    const void *dob, const float *lseb, const float *delta, float *dq_acc,
                                    void *dkb, void *dvb, hipStream_t st);
+// bf16 branch-local kernels on 16x16 MFMA. Forward: with o_pre non-NULL it
+// merges with the main-prefix partial and writes ob/lseb, else it writes the
+// float32 partial o_loc/lse_loc. Backward: writes dqb = dq_acc (main part) +
+// the branch-local part, and dkb, dvb.
+hipError_t launch_branch_fwd_bf16(const Meta &mt, const bf16 *qb, const bf16 *kb, const bf16 *vb,
+                                  const float *o_pre, const float *lse_pre, float *o_loc, float *lse_loc, bf16 *ob,
+                                  float *lseb, hipStream_t st);
+hipError_t launch_branch_bwd_bf16(const Meta &mt, const bf16 *qb, const bf16 *kb, const bf16 *vb, const bf16 *dob,
+                                  const float *lseb, const float *delta, const float *dq_acc, bf16 *dqb, bf16 *dkb,
+                                  bf16 *dvb, hipStream_t st);
 hipError_t launch_bwd_preprocess(const Meta &mt, ba_dtype_t dt, const void *o, const void *d_o, const void *ob,
                                  const void *d_ob, float *delta, hipStream_t st);
 hipError_t launch_convert_rows(const float *acc, int64_t n, void *out, ba_dtype_t dt, hipStream_t st);

@@ -105,10 +105,12 @@ ba_status_t validate_and_copy(const ba_problem_t *p, ba_plan *pl) {
       pl->cu_branch[m] = (int32_t)v;
     }
   }
+  pl->max_branch = 0;
   for (int64_t m = 0; m < pl->A; ++m) {
     int32_t L = pl->cu_branch[m + 1] - pl->cu_branch[m];
     if (L < 0) return set_error(BA_EINVAL, "cu_branch must be non-decreasing");
     if (L > kMaxBranch) return set_error(BA_EINVAL, "a branch has more than 32 rows");
+    pl->max_branch = std::max(pl->max_branch, L);
   }
   pl->Rb = pl->cu_branch[pl->A];
   pl->mode.resize(pl->A);
@@ -314,7 +316,9 @@ void build(ba_plan *pl) {
   pl->off_lse_pre = pl->off_o_pre + o_bytes;
   pl->off_o_loc = pl->off_lse_pre + l_bytes;
   pl->off_lse_loc = pl->off_o_loc + o_bytes;
-  pl->ws_fwd = pl->off_lse_loc + l_bytes;
+  // bf16: the branch-local kernel merges in registers, so the forward needs no
+  // branch-local partial.
+  pl->ws_fwd = pl->dtype == BA_BF16 ? pl->off_o_loc : pl->off_lse_loc + l_bytes;
   pl->off_delta = base;
   size_t d_bytes = align_up((size_t)R * pl->hq * f32, 256);
   pl->off_dq_acc = pl->off_delta + d_bytes;

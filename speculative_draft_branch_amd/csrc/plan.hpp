@@ -74,6 +74,7 @@ struct ba_plan {
   std::vector<int32_t> cu, q_pos, anchors, cu_branch;
   std::vector<uint8_t> mode;
   int32_t rows_per_tile;  // base rows per query tile
+  int32_t max_branch;     // longest branch (rows of one anchor)
   int32_t n_qtiles, n_ktiles, n_fwd_pairs, n_vt_tiles;
   int64_t pairs[3];
   ba::BlobLayout layout;

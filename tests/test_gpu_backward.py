@@ -50,6 +50,9 @@ EDGE = {
     "nobranch_bf16_d128": lambda: custom("n", "bf16", 8, 8, 128, [129, 1, 64, 200], None, [], [], [], seed=4),
     "branches_only_bf16": lambda: custom("b", "bf16", 4, 1, 128, [90], [], [0, 17, 89], [5, 16, 32],
                                          [TTT, BLOCK, TTT], seed=4),
+    # branches longer than 16 rows in both modes at GQA 8:1, d=64 (two 16-key blocks per branch)
+    "long_branches_bf16_d64": lambda: custom("l", "bf16", 16, 2, 64, [120, 60], None, [0, 40, 119, 130, 179],
+                                             [17, 32, 20, 24, 9], [BLOCK, BLOCK, TTT, TTT, BLOCK], std=1.0, seed=4),
 }
 
 DENSE = ["tiny_f32", "qwen3_8b_16k_div16", "ctx256k_rank3_chunk64", "ctx256k_rank3_chunk80", "dflash_64k_1024",

@@ -70,6 +70,9 @@ EDGE = {
     "peaked_bf16_d128": lambda: _edge("p", "bf16", 128, 4, 2, [300, 211], None, list(range(0, 511, 3)),
                                       [7] * len(range(0, 511, 3)), [TTT] * len(range(0, 511, 3)), std=0.5,
                                       qk_scale=4.0),
+    # branches longer than 16 rows in both modes at GQA 8:1, d=64 (two 16-key blocks per branch)
+    "long_branches_bf16_d64": lambda: _edge("l", "bf16", 64, 16, 2, [120, 60], None, [0, 40, 119, 130, 179],
+                                            [17, 32, 20, 24, 9], [BLOCK, BLOCK, TTT, TTT, BLOCK]),
     "peaked_bf16_d64": lambda: _edge("p", "bf16", 64, 16, 2, [700], None, list(range(0, 700, 16)),
                                      [16] * len(range(0, 700, 16)), [BLOCK] * len(range(0, 700, 16)), std=0.5,
                                      qk_scale=4.0),

@@ -107,7 +107,9 @@ def test_workspace_sizes_cover_partials():
     w = W.get("ctx256k_rank3_chunk64")
     p = Plan.from_workload(w)
     f32 = 4
-    assert p.workspace_bytes(0) >= 2 * w.Rb * w.num_q_heads * w.head_dim * f32
+    partial = w.Rb * w.num_q_heads * (w.head_dim + 1) * f32  # one float32 (O, LSE) partial of the branch rows
+    # bf16 merges the branch-local part in registers: only the main-prefix partial is stored
+    assert partial <= p.workspace_bytes(0) < 2 * partial
     assert p.workspace_bytes(1) >= (w.Nq + w.Rb) * w.num_q_heads * (w.head_dim + 1) * f32
     assert 0 < p.workspace_bytes(2) <= p.workspace_bytes(0)
 
