@@ -15,7 +15,9 @@ softmaxes with the log-sum-exp reduction (evolve.pub review, "Scope & Claims":
 branch attention under CP, the online-softmax reduction of Eq. 2; rcap.io
 explainer, paragraph on branch attention under context parallelism).  The
 split itself is also written out here (``split_forward``) so tests can check
-that split-then-merge equals the union softmax.
+that split-then-merge equals the union softmax, and so is the ring form of the
+main-key part (``ring_forward``: key windows merged one after another, as a
+context-parallel ring delivers them).
 
 Arithmetic is float64 unless a caller asks otherwise.
 
@@ -34,5 +36,5 @@ finite differences, invariants).
 """
 from .branch_attention import (  # noqa: F401
     TTT, BLOCK, Problem, row_keys, dense_mask, attend, attend_bwd, forward, backward,
-    forward_rows, backward_rows, lse_merge, split_forward, pair_counts,
+    forward_rows, backward_rows, lse_merge, split_forward, ring_forward, pair_counts,
 )

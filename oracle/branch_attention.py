@@ -411,6 +411,37 @@ def split_forward(p: Problem, t: Dict[str, np.ndarray], dtype=np.float64):
     return merged, part
 
 
+def ring_forward(p: Problem, t: Dict[str, np.ndarray], windows, dtype=np.float64):
+    """Main-key part of every row computed the way a context-parallel ring
+    computes it: the main keys arrive in windows [lo, hi) of packed positions;
+    for each window every row (main and branch) attends the keys of its causal
+    main prefix that fall inside it, and that partial joins a running (O, LSE)
+    through ``lse_merge``, in the order given (rcap.io explainer: ring attention
+    passes K/V chunks between ranks and combines the partial results by the
+    log-sum-exp step; evolve.pub review, section 3.2 and Eq. 2).
+
+    Windows may be empty, overlap [0, N) only in part, or lie past N; when they
+    tile [0, N) without overlap the result is the main-key partial of every row.
+    Returns o_run [Nq+Rb, Hq, d] and lse_run [Hq, Nq+Rb] (rows: main, then branch).
+    """
+    R, N = p.Nq + p.Rb, p.N
+    Q = np.concatenate([_as(t["q"], dtype), _as(t["qb"], dtype)])
+    main_mask = np.zeros((R, N), dtype=bool)
+    for r in range(R):
+        lo, hi, _ = row_keys(p, r)
+        main_mask[r, lo:hi + 1] = True
+    o_run = np.zeros((R, p.hq, p.d), dtype)
+    lse_run = np.full((p.hq, R), -np.inf, dtype)
+    for lo, hi in windows:
+        lo, hi = max(int(lo), 0), min(int(hi), N)
+        if hi <= lo:
+            continue
+        o_w, l_w = attend(Q, _as(t["k"][lo:hi], dtype), _as(t["v"][lo:hi], dtype), main_mask[:, lo:hi],
+                          p.kv_head_of, p.scale, dtype)
+        o_run, lse_run = lse_merge(o_run, lse_run, o_w, l_w)
+    return o_run, lse_run
+
+
 def pair_counts(p: Problem) -> Dict[str, int]:
     """Visible (row, key) pairs per head: main rows x main keys, branch rows x
     main keys, branch rows x branch keys."""

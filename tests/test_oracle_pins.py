@@ -285,6 +285,50 @@ def test_three_way_split_matches_union():
         np.testing.assert_allclose(l, f["lseb"], atol=1e-12)
 
 
+def _main_partials(p, t):
+    _, part = oracle.split_forward(p, t)
+    return (np.concatenate([part["o_main"], part["ob_main"]]),
+            np.concatenate([part["lse_main"], part["lseb_main"]], axis=1))
+
+
+@pytest.mark.parametrize("name", ["mixed", "blocks", "single_tokens"])
+def test_ring_windows_merge_to_the_single_pass(name):
+    """Key windows that tile [0, N), merged in any order (with empty windows and
+    windows past N mixed in), give the main-key partial of every row."""
+    w = _case(name)
+    p = Problem.from_workload(w)
+    t = _f64(make_inputs(w))
+    o_ref, l_ref = _main_partials(p, t)
+    cuts = [0, 3, 4, 9, 10, p.N]
+    wins = [(a, b) for a, b in zip(cuts[:-1], cuts[1:]) if a < b]
+    rng = np.random.default_rng(5)
+    for order in (wins, wins[::-1], [wins[i] for i in rng.permutation(len(wins))]):
+        o, l = oracle.ring_forward(p, t, list(order) + [(2, 2), (p.N, p.N + 7)])
+        np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l, l_ref, rtol=0, atol=1e-12)
+
+
+def test_ring_zigzag_steps_and_a_missing_window():
+    """The zigzag layout of a CP=4 ring (8 chunks; rank r holds chunks r and 7-r)
+    delivered to rank 1 in ring order reproduces the single pass; leaving one
+    chunk out changes every row that sees it."""
+    w = _tiny("zz", hq=2, hkv=1, d=8, seqs=(32,), q_pos=list(range(4, 8)) + list(range(24, 28)),
+              anchors=(5, 24, 27), lens=(3, 2, 4), modes=(TTT, BLOCK, TTT))
+    p = Problem.from_workload(w)
+    t = _f64(make_inputs(w))
+    o_ref, l_ref = _main_partials(p, t)
+    steps = [(r, 7 - r) for r in (1, 0, 3, 2)]  # chunk pairs in the order the ring brings them
+    wins = [(4 * c, 4 * c + 4) for pair in steps for c in pair]
+    o, l = oracle.ring_forward(p, t, wins)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, l_ref, rtol=0, atol=1e-12)
+    o2, l2 = oracle.ring_forward(p, t, [x for x in wins if x != (8, 12)])
+    sees = np.array([oracle.row_keys(p, r)[1] >= 8 for r in range(p.Nq + p.Rb)])
+    assert sees.any()
+    assert np.all(np.abs(l2 - l_ref)[:, sees] > 1e-6)
+    np.testing.assert_allclose(l2[:, ~sees], l_ref[:, ~sees], atol=1e-12)
+
+
 # --------------------------------------------------------------------------
 # locality: branch rows depend only on their anchor's prefix and their own branch
 
