@@ -167,6 +167,30 @@ ba_status_t ba_branch_local_fwd(const ba_plan_t *plan, const void *qb, const voi
                                 float *o_loc, float *lse_loc,
                                 void *workspace, size_t ws_bytes, void *stream);
 
+/* One step of a context-parallel ring, forward, main keys only (evolve.pub
+ * review, section 3.2 and Eq. 2; rcap.io explainer, ring attention: each rank
+ * receives a chunk of the main K/V per step and merges the partial result by
+ * the log-sum-exp step). Every row -- main rows 0..Nq-1, then branch rows
+ * Nq..Nq+Rb-1 -- attends the main keys of its causal prefix whose packed
+ * positions lie in the window [win_lo, win_hi), and that partial is merged
+ * into the running float32 result in place:
+ *   o_run [Nq+Rb, Hq, d], lse_run [Hq, Nq+Rb] (natural-log LSE).
+ * Start from o_run = 0, lse_run = -inf. After steps whose windows tile [0, N),
+ * in any order, o_run/lse_run equal ba_main_fwd's o, lse (main rows) and
+ * o_pre, lse_pre (branch rows) up to rounding; the branch-local part is not
+ * included (it never leaves the rank) and joins with lse_merge.
+ * k_win, v_win: bf16 [win_hi - win_lo, Hkv, d], the K/V rows of the window
+ * only (row 0 = position win_lo), as a ring delivers them. The window need not
+ * align with sequences or tiles. A row that sees no key of the window keeps
+ * its running value; an empty window (win_lo == win_hi) enqueues nothing.
+ * Rows are updated without atomics: calls that overlap on one o_run race.
+ * BA_BF16 plans only (BA_EUNSUPPORTED otherwise); BA_EINVAL unless
+ * 0 <= win_lo <= win_hi <= N. workspace: ws_bytes >= ba_workspace_bytes(plan, 2). */
+ba_status_t ba_ring_step_fwd(const ba_plan_t *plan, const void *q, const void *qb,
+                             const void *k_win, const void *v_win, int64_t win_lo, int64_t win_hi,
+                             float *o_run, float *lse_run,
+                             void *workspace, size_t ws_bytes, void *stream);
+
 /* Opt-in per-kernel timing for profiling: while enabled, every kernel launch
  * and metadata upload of the library is bracketed by HIP events recorded on the
  * call's stream. ba_timing_read() waits for the recorded events (not for the

@@ -73,6 +73,8 @@ def _load():
     L.ba_main_fwd.restype = st
     L.ba_branch_local_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.ba_branch_local_fwd.restype = st
+    L.ba_ring_step_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, sz, vp]
+    L.ba_ring_step_fwd.restype = st
     L.ba_status_str.argtypes = [st]
     L.ba_status_str.restype = C.c_char_p
     L.ba_last_error.argtypes = []
@@ -102,6 +104,7 @@ def abi_version() -> int:
 def exported_symbols() -> list:
     return ["ba_plan_create", "ba_plan_destroy", "ba_workspace_bytes", "ba_plan_sizes", "ba_plan_pairs",
             "branch_attn_fwd", "branch_attn_bwd", "lse_merge", "ba_main_fwd", "ba_branch_local_fwd",
+            "ba_ring_step_fwd",
             "ba_status_str", "ba_last_error", "ba_abi_version", "ba_timing_enable", "ba_timing_reset",
             "ba_timing_kernels", "ba_timing_kernel_name", "ba_timing_read"]
 

@@ -15,11 +15,11 @@ namespace {
 // Opt-in per-kernel timing: HIP events recorded on the launch stream.
 enum KernelId {
   K_UPLOAD = 0, K_MAIN_FWD, K_BRANCH_LOCAL_FWD, K_LSE_MERGE, K_BWD_PREPROCESS, K_MAIN_BWD_DQ, K_MAIN_BWD_DKDV,
-  K_BRANCH_LOCAL_BWD, K_DQ_CONVERT, K_VT_TRANSPOSE, K_COUNT
+  K_BRANCH_LOCAL_BWD, K_DQ_CONVERT, K_VT_TRANSPOSE, K_RING_FWD, K_COUNT
 };
 const char *kKernelNames[K_COUNT] = {"metadata_upload", "main_fwd", "branch_local_fwd", "lse_merge",
                                      "bwd_preprocess", "main_bwd_dq", "main_bwd_dkdv", "branch_local_bwd",
-                                     "dq_convert",      "vt_transpose"};
+                                     "dq_convert",      "vt_transpose", "ring_step_fwd"};
 
 struct TimingState {
   std::mutex mu;
@@ -230,6 +230,35 @@ ba_status_t ba_branch_local_fwd(const ba_plan_t *pl, const void *qb, const void 
     return launch_branch_local_fwd(mt, pl->dtype, qb, kb, vb, o_loc, lse_loc, st);
   }));
   return BA_OK;
+}
+
+ba_status_t ba_ring_step_fwd(const ba_plan_t *pl, const void *q, const void *qb, const void *k_win,
+                             const void *v_win, int64_t win_lo, int64_t win_hi, float *o_run, float *lse_run,
+                             void *workspace, size_t ws_bytes, void *stream) {
+  BA_TRY(check_plan(pl));
+  if (pl->dtype != BA_BF16) return set_error(BA_EUNSUPPORTED, "ba_ring_step_fwd: bf16 only");
+  if (win_lo < 0 || win_lo > win_hi || win_hi > pl->N)
+    return set_error(BA_EINVAL, "ba_ring_step_fwd: need 0 <= win_lo <= win_hi <= N");
+  const int64_t hd = (int64_t)pl->hq * pl->d, kd = (int64_t)pl->hkv * pl->d, R = pl->Nq + pl->Rb;
+  BA_TRY(check_ptr(q, pl->Nq * hd, "q"));
+  BA_TRY(check_ptr(qb, pl->Rb * hd, "qb"));
+  BA_TRY(check_ptr(k_win, (win_hi - win_lo) * kd, "k_win"));
+  BA_TRY(check_ptr(v_win, (win_hi - win_lo) * kd, "v_win"));
+  BA_TRY(check_ptr(o_run, R * hd, "o_run"));
+  BA_TRY(check_ptr(lse_run, R * pl->hq, "lse_run"));
+  BA_TRY(check_ws(pl, workspace, ws_bytes, 2));
+  if (win_lo == win_hi) return BA_OK;  // an empty window is the identity
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  BA_TRY(upload(pl, workspace, st));
+  const Meta mt = make_meta(pl, workspace);
+  bf16 *vt = reinterpret_cast<bf16 *>(static_cast<uint8_t *>(workspace) + pl->off_vt);
+  BA_TRY(timed(K_VT_TRANSPOSE, st, "V transpose (window)", [&] {
+    return launch_vt_transpose_bf16(mt, (const bf16 *)v_win, vt, st, (int)win_lo, (int)win_hi);
+  }));
+  return timed(K_RING_FWD, st, "ring step forward", [&] {
+    return launch_ring_fwd_bf16(mt, (const bf16 *)q, (const bf16 *)qb, (const bf16 *)k_win, vt, (int)win_lo,
+                                (int)win_hi, o_run, lse_run, st);
+  });
 }
 
 ba_status_t lse_merge(int64_t rows, int32_t heads, int32_t head_dim, const float *o_a, const float *lse_a,

@@ -290,6 +290,24 @@ struct AsyncTile {
       }
     }
   }
+  // As load(), for a tile that may also begin before row `first` (k0 may be
+  // negative): rows outside [first, last] read the nearer of the two.
+  __device__ __forceinline__ void load_window(bf16 *lds, const bf16 *__restrict__ base, int k0, int first,
+                                              int last) const {
+    if (k0 >= first) {
+      load(lds, base, k0, last);
+      return;
+    }
+    const char *b = reinterpret_cast<const char *>(base);
+#pragma unroll
+    for (int it = 0; it < PER_WAVE; ++it) {
+      const int r = min(max(k0 + row[it], first), last);
+      const uint32_t chunk = off[it] - (uint32_t)(row[it] * row_stride) * 2u;  // byte offset within the row
+      __builtin_amdgcn_global_load_lds(b + (int64_t)r * row_stride * 2 + chunk,
+                                       (__attribute__((address_space(3))) void *)(lds + (lds_block + it) * 512),
+                                       16, 0, 0);
+    }
+  }
 };
 
 template <int HD, int ROWS, int NT>

@@ -37,9 +37,17 @@ hipError_t launch_main_bwd_f32(const Meta &mt, const float *q, const float *qb, 
 // bf16 MFMA main-sequence kernels
 // V^T tiles of each sequence: [tile][Hkv][d][64 keys], keys of each 16-key group
 // stored in MFMA operand-slot order; keys past the sequence end are zero.
-hipError_t launch_vt_transpose_bf16(const Meta &mt, const bf16 *v, bf16 *vt, hipStream_t st);
+// With win_lo < win_hi (a ring step) only the tiles meeting [win_lo, win_hi) are
+// written, from v holding the window's rows (row 0 = position win_lo).
+hipError_t launch_vt_transpose_bf16(const Meta &mt, const bf16 *v, bf16 *vt, hipStream_t st, int win_lo = 0,
+                                    int win_hi = 0);
 hipError_t launch_main_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *vt,
                                 bf16 *o, float *lse, float *o_pre, float *lse_pre, hipStream_t st);
+// One ring step: every row against the main keys of its prefix inside
+// [win_lo, win_hi) (k_win: those rows only; vt: their V^T tiles), merged into
+// the running float32 o_run [Nq+Rb][Hq][d] / lse_run [Hq][Nq+Rb].
+hipError_t launch_ring_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k_win, const bf16 *vt,
+                                int win_lo, int win_hi, float *o_run, float *lse_run, hipStream_t st);
 hipError_t launch_main_bwd_dq_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *v,
                                    const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
                                    const float *delta, float *dq_acc, hipStream_t st);

@@ -50,6 +50,7 @@ struct FwdState {
   float m_run, l_run;
   bool started;  // the running max has been set (wave-uniform)
   int end, wmin, wmax;
+  int klo;  // ring step: first key of the window (keys below it are masked)
   int lane;
   uint32_t k_base, k_t;  // K row reads
   uint32_t v_base, v_t;  // V^T row reads
@@ -135,17 +136,18 @@ __device__ __forceinline__ float fwd_form_p(const FwdState<HD> &st, const f32x16
   return rs;
 }
 
-template <int HD>
+template <int HD, bool RING>
 __device__ __forceinline__ void fwd_softmax(FwdState<HD> &st, f32x16 (&s)[2], int k0, float sl2, bf16x8 (&pb)[4]) {
   constexpr int DT = FwdState<HD>::DT;
   const int lane = st.lane;
-  if (k0 + 63 > st.wmin) {  // some key of this tile lies past some row's prefix end
+  // some key of this tile lies past some row's prefix end (or, in a ring step, before the window)
+  if (k0 + 63 > st.wmin || (RING && k0 < st.klo)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = k0 + kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-        if (key > st.end) s[kb][i] = -INFINITY;
+        if (key > st.end || (RING && key < st.klo)) s[kb][i] = -INFINITY;
       }
   }
   if (!st.started) {  // the wave's first tile holds every row's first visible key
@@ -166,15 +168,29 @@ __device__ __forceinline__ void fwd_softmax(FwdState<HD> &st, f32x16 (&s)[2], in
 }
 
 
+// K tile of keys [key0, key0 + 64): rows past `last` read row `last`; in a ring
+// step the buffer starts at position kb0 and rows before `first` read `first`.
+template <bool RING, class Tile>
+__device__ __forceinline__ void load_k_tile(const Tile &kt, bf16 *dst, const bf16 *kg, int key0, int kb0, int first,
+                                            int last) {
+  if constexpr (RING) kt.load_window(dst, kg, key0 - kb0, first - kb0, last - kb0);
+  else kt.load(dst, kg, key0, last);
+}
+
 }  // namespace
 
-template <int HD>
+// RING: one step of a context-parallel ring. Only the main keys in the window
+// [win_lo, win_hi) are attended; k holds exactly those rows (row 0 = position
+// win_lo) and vt their V^T tiles; every row's partial is merged into the
+// running float32 (o_run [Nq+Rb][Hq][d], lse_run [Hq][Nq+Rb]) in the epilogue.
+template <int HD, bool RING>
 __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
                                                             const bf16 *__restrict__ qb,
                                                             const bf16 *__restrict__ k,
                                                             const bf16 *__restrict__ vt, bf16 *__restrict__ o,
                                                             float *__restrict__ lse, float *__restrict__ o_pre,
-                                                            float *__restrict__ lse_pre) {
+                                                            float *__restrict__ lse_pre, int win_lo, int win_hi,
+                                                            float *__restrict__ o_run, float *__restrict__ lse_run) {
   constexpr int BN = 64;  // keys per K/V tile
   constexpr int KS = HD / 16, DT = HD / 32;
   __shared__ __attribute__((aligned(16))) bf16 sK0[BN * HD];
@@ -190,8 +206,18 @@ __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf
   const int ta = uni(mt.fwd_pairs[2 * pair]), tb = uni(mt.fwd_pairs[2 * pair + 1]);
   const QTile tile_a = load_qtile(mt.qtiles + ta);
   const int end_b = tb >= 0 ? uni(mt.qtiles[tb].end_max) : -1;
-  const int kv_lo = tile_a.kv_lo, kv_end = max(tile_a.end_max, end_b);
-  const int ntiles = (kv_end - kv_lo + BN) / BN;
+  // Keys [k_first + 64j, ...) for j < ntiles; k_first is the sequence start, or
+  // in a ring step the start of the sequence's 64-key tile holding the window
+  // start (tile t0 of the sequence), and keys before klo are masked.
+  const int kv_lo = tile_a.kv_lo;
+  int kv_end = max(tile_a.end_max, end_b), klo = kv_lo, t0 = 0;
+  if constexpr (RING) {
+    klo = max(kv_lo, win_lo);
+    t0 = (klo - kv_lo) / BN;
+    kv_end = min(kv_end, win_hi - 1);
+  }
+  const int k_first = kv_lo + t0 * BN;
+  const int ntiles = kv_end >= klo ? (kv_end - k_first + BN) / BN : 0;
 
   // This lane's query row: MFMA row 32*(wave%4) + lane%32 = base row * G + head
   // of the group's tile.
@@ -206,6 +232,7 @@ __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf
     if (bi < tile.nrows) {
       row = mt.tile_row_id[tile.row_begin + bi];
       st.end = mt.tile_row_end[tile.row_begin + bi];
+      if constexpr (RING) st.end = min(st.end, win_hi - 1);  // may fall below klo: the row sees no key
     }
   }
   const int h = mt.group_heads[g * G + hj];
@@ -224,6 +251,7 @@ __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf
   }
   st.wmin = wave_min(row >= 0 ? st.end : INT_MAX);
   st.wmax = wave_max(st.end);
+  st.klo = klo;
   st.m_run = -INFINITY;
   st.l_run = 0.0f;
   st.started = false;
@@ -241,9 +269,12 @@ __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf
   AsyncTile<64, HD, 512> vtt;
   vtt.init(64, tid);
   const bf16 *kg = k + (int64_t)g * HD;
-  const bf16 *vtg = vt + ((int64_t)mt.vt_base[tile_a.seq] * hkv + g) * (HD * 64);
+  const bf16 *vtg = vt + ((int64_t)(mt.vt_base[tile_a.seq] + t0) * hkv + g) * (HD * 64);
   const int64_t vt_stride = (int64_t)hkv * HD * 64;  // between consecutive V^T tiles
-  kt.load(sK0, kg, kv_lo, kv_end);
+  // K rows are addressed relative to the buffer's first position (the window
+  // start in a ring step); a ring step's first tile may begin before it.
+  const int kb0 = RING ? win_lo : 0;
+  if (ntiles > 0) load_k_tile<RING>(kt, sK0, kg, k_first, kb0, klo, kv_end);
   dma_barrier<0>();
 
   // Phase slots: slot t runs, for group grpi, local phase u = t - grpi; even u
@@ -263,14 +294,14 @@ __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf
       bf16 *const sVc = par ? sV1 : sV0, *const sVp = par ? sV0 : sV1;
       // slot 2jj: requests, then group 0 matrix phase of jj, group 1 softmax of jj-1
       if (2 * jj >= nslots) goto done;
-      if (jj + 1 < ntiles) kt.load(sKn, kg, kv_lo + (jj + 1) * BN, kv_end);
+      if (jj + 1 < ntiles) load_k_tile<RING>(kt, sKn, kg, k_first + (jj + 1) * BN, kb0, klo, kv_end);
       if (jj < ntiles) vtt.load(sVc, vtg + jj * vt_stride, 0, HD - 1);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         if (h2 == 1 && 2 * jj + 1 >= nslots) goto done;
         if (grpi == h2) {  // matrix phase of tile jj
-          const bool do_pv = jj >= 1 && jj <= ntiles && kv_lo + (jj - 1) * BN <= st.wmax;
-          const bool do_s = jj < ntiles && kv_lo + jj * BN <= st.wmax;
+          const bool do_pv = jj >= 1 && jj <= ntiles && k_first + (jj - 1) * BN <= st.wmax;
+          const bool do_s = jj < ntiles && k_first + jj * BN <= st.wmax;
           __builtin_amdgcn_s_setprio(1);  // the matrix wave wins issue arbitration over the softmax wave
           if (do_pv && do_s) fwd_mphase<HD, true, true>(st, sVp, sKc, pb, s);
           else if (do_s) fwd_mphase<HD, false, true>(st, sVp, sKc, pb, s);
@@ -278,7 +309,8 @@ __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf
           __builtin_amdgcn_s_setprio(0);
         } else {  // softmax of tile jj - 1 (group 1 at h2 = 0) or jj (group 0 at h2 = 1)
           const int js = jj - 1 + h2;
-          if (js >= 0 && js < ntiles && kv_lo + js * BN <= st.wmax) fwd_softmax<HD>(st, s, kv_lo + js * BN, sl2, pb);
+          if (js >= 0 && js < ntiles && k_first + js * BN <= st.wmax)
+            fwd_softmax<HD, RING>(st, s, k_first + js * BN, sl2, pb);
         }
         if (h2 == 0) dma_barrier<63>();
         else dma_barrier<0>();
@@ -288,6 +320,32 @@ __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf
 done:
 
   const float l_tot = half_sum(st.l_run);
+  if constexpr (RING) {
+    // Merge this window's partial into the running (O, LSE) of the row (Eq. 2);
+    // a row that saw no key of the window leaves it unchanged.
+    if (row >= 0 && l_tot > 0.0f) {
+      const int64_t R = mt.Nq + mt.Rb;
+      float *orow = o_run + ((int64_t)row * mt.hq + h) * HD;
+      const float lp = (st.m_run + __log2f(l_tot)) * kLn2;
+      const float la = lse_run[(int64_t)h * R + row];
+      const float M = fmaxf(la, lp);
+      const float wa = __expf(la - M), wb = __expf(lp - M);
+      const float tot = wa + wb;
+      const float fa = wa / tot, fb = wb / (tot * l_tot);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = dt * 32 + q4 * 8 + (lane >> 5) * 4;
+          const f32x4 x = *reinterpret_cast<const f32x4 *>(orow + d);
+          const f32x4 val = {fa * x[0] + fb * st.acc[dt][q4 * 4 + 0], fa * x[1] + fb * st.acc[dt][q4 * 4 + 1],
+                             fa * x[2] + fb * st.acc[dt][q4 * 4 + 2], fa * x[3] + fb * st.acc[dt][q4 * 4 + 3]};
+          *reinterpret_cast<f32x4 *>(orow + d) = val;
+        }
+      if (lane < 32) lse_run[(int64_t)h * R + row] = M + __logf(tot);
+    }
+    return;
+  }
   if (row >= 0) {
     const float inv = 1.0f / l_tot;
 #pragma unroll
@@ -315,18 +373,29 @@ done:
 // V^T tile: 64 keys of one sequence (zero past its end) x d, written as d rows
 // of 64 keys with bits 2 and 3 of the key index swapped inside each 16-key
 // group (stored position 8h + 4c + j holds key 8c + 4h + j).
+// Ring step (win_lo < win_hi): only tiles that meet the window are written, v
+// holds the window's rows (row 0 = position win_lo) and keys outside the window
+// are zero.
 template <int HD>
 __global__ __launch_bounds__(256) void vt_transpose_bf16_kernel(Meta mt, const bf16 *__restrict__ v,
-                                                                bf16 *__restrict__ vt) {
+                                                                bf16 *__restrict__ vt, int win_lo, int win_hi) {
   constexpr int NCH = HD / 8;
   constexpr int LD = HD + 2;  // padded LDS row (elements) against bank conflicts on the column reads
   __shared__ __attribute__((aligned(16))) bf16 t[64 * LD];
   const int hkv = mt.hkv, g = blockIdx.x % hkv, ti = blockIdx.x / hkv;
-  const int key_lo = mt.vt_tiles[2 * ti], key_hi = mt.vt_tiles[2 * ti + 1];
+  const int key_lo = mt.vt_tiles[2 * ti];
+  int lo = key_lo, hi = mt.vt_tiles[2 * ti + 1], base = 0;
+  if (win_lo < win_hi) {
+    lo = max(lo, win_lo);
+    hi = min(hi, win_hi);
+    base = win_lo;
+    if (lo >= hi) return;  // the whole workgroup
+  }
   for (int c = threadIdx.x; c < 64 * NCH; c += 256) {
     const int r = c / NCH, ch = c % NCH;
+    const int key = key_lo + r;
     uint4 x = {0u, 0u, 0u, 0u};
-    if (key_lo + r < key_hi) x = *reinterpret_cast<const uint4 *>(v + ((int64_t)(key_lo + r) * hkv + g) * HD + ch * 8);
+    if (key >= lo && key < hi) x = *reinterpret_cast<const uint4 *>(v + ((int64_t)(key - base) * hkv + g) * HD + ch * 8);
     uint32_t *d32 = reinterpret_cast<uint32_t *>(t + r * LD + ch * 8);
     d32[0] = x.x;
     d32[1] = x.y;
@@ -348,13 +417,27 @@ __global__ __launch_bounds__(256) void vt_transpose_bf16_kernel(Meta mt, const b
   }
 }
 
-hipError_t launch_vt_transpose_bf16(const Meta &mt, const bf16 *v, bf16 *vt, hipStream_t st) {
+// Every variant is instantiated explicitly: with two values of the bool
+// parameter launched from this file, this hipcc emitted the host launch stubs
+// of only one of them (the other launch then referenced an undefined stub).
+#define BA_FWD_INSTANCE(HD, RING)                                                                                \
+  template __global__ void main_fwd_bf16_kernel<HD, RING>(Meta, const bf16 *, const bf16 *, const bf16 *,        \
+                                                          const bf16 *, bf16 *, float *, float *, float *, int, int, \
+                                                          float *, float *)
+BA_FWD_INSTANCE(128, false);
+BA_FWD_INSTANCE(64, false);
+BA_FWD_INSTANCE(128, true);
+BA_FWD_INSTANCE(64, true);
+#undef BA_FWD_INSTANCE
+
+hipError_t launch_vt_transpose_bf16(const Meta &mt, const bf16 *v, bf16 *vt, hipStream_t st, int win_lo,
+                                    int win_hi) {
   if (mt.n_vt_tiles == 0) return hipSuccess;
   const unsigned grid = (unsigned)((int64_t)mt.n_vt_tiles * mt.hkv);
   if (mt.d == 128)
-    vt_transpose_bf16_kernel<128><<<grid, 256, 0, st>>>(mt, v, vt);
+    vt_transpose_bf16_kernel<128><<<grid, 256, 0, st>>>(mt, v, vt, win_lo, win_hi);
   else
-    vt_transpose_bf16_kernel<64><<<grid, 256, 0, st>>>(mt, v, vt);
+    vt_transpose_bf16_kernel<64><<<grid, 256, 0, st>>>(mt, v, vt, win_lo, win_hi);
   return hipGetLastError();
 }
 
@@ -363,9 +446,24 @@ hipError_t launch_main_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, c
   if (mt.n_fwd_pairs == 0) return hipSuccess;
   const unsigned grid = (unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv);
   if (mt.d == 128)
-    main_fwd_bf16_kernel<128><<<grid, 512, 0, st>>>(mt, q, qb, k, vt, o, lse, o_pre, lse_pre);
+    main_fwd_bf16_kernel<128, false><<<grid, 512, 0, st>>>(mt, q, qb, k, vt, o, lse, o_pre, lse_pre, 0, 0, nullptr,
+                                                           nullptr);
   else
-    main_fwd_bf16_kernel<64><<<grid, 512, 0, st>>>(mt, q, qb, k, vt, o, lse, o_pre, lse_pre);
+    main_fwd_bf16_kernel<64, false><<<grid, 512, 0, st>>>(mt, q, qb, k, vt, o, lse, o_pre, lse_pre, 0, 0, nullptr,
+                                                          nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k_win, const bf16 *vt,
+                                int win_lo, int win_hi, float *o_run, float *lse_run, hipStream_t st) {
+  if (mt.n_fwd_pairs == 0 || win_lo >= win_hi) return hipSuccess;
+  const unsigned grid = (unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv);
+  if (mt.d == 128)
+    main_fwd_bf16_kernel<128, true><<<grid, 512, 0, st>>>(mt, q, qb, k_win, vt, nullptr, nullptr, nullptr, nullptr,
+                                                          win_lo, win_hi, o_run, lse_run);
+  else
+    main_fwd_bf16_kernel<64, true><<<grid, 512, 0, st>>>(mt, q, qb, k_win, vt, nullptr, nullptr, nullptr, nullptr,
+                                                         win_lo, win_hi, o_run, lse_run);
   return hipGetLastError();
 }
 

@@ -105,6 +105,22 @@ def ba_branch_local_fwd(plan: Plan, qb, kb, vb, o_loc, lse_loc, ws: torch.Tensor
                                   _stream()), "ba_branch_local_fwd")
 
 
+def ba_ring_step_fwd(plan: Plan, q, qb, k_win, v_win, win_lo: int, win_hi: int, o_run, lse_run, ws: torch.Tensor):
+    """One ring step: every row against the main keys of its prefix in [win_lo, win_hi),
+    merged into the running float32 (o_run [Nq+Rb, Hq, d], lse_run [Hq, Nq+Rb]) in place."""
+    dt, s = _DT[plan.dtype], _shapes(plan)
+    _chk(q, "q", dt, s["q"])
+    _chk(qb, "qb", dt, s["qb"])
+    win = (int(win_hi) - int(win_lo),) + tuple(s["k"][1:])
+    _chk(k_win, "k_win", dt, win)
+    _chk(v_win, "v_win", dt, win)
+    rows = s["q"][0] + s["qb"][0]
+    _chk(o_run, "o_run", torch.float32, (rows,) + tuple(s["q"][1:]))
+    _chk(lse_run, "lse_run", torch.float32, (s["q"][1], rows))
+    check(lib.ba_ring_step_fwd(plan.handle, _p(q), _p(qb), _p(k_win), _p(v_win), int(win_lo), int(win_hi), _p(o_run),
+                               _p(lse_run), _p(ws), ws.numel(), _stream()), "ba_ring_step_fwd")
+
+
 def fwd(plan: Plan, q, k, v, qb, kb, vb, ws: Optional[torch.Tensor] = None):
     """Allocating convenience form: returns (o, lse, ob, lseb)."""
     dev = q.device

@@ -146,3 +146,22 @@ def test_entry_points_reject_bad_arguments_without_touching_the_gpu():
     assert lib.branch_attn_fwd(p.handle, *bad, fake, p.workspace_bytes(0), None) == BA_EINVAL
     assert lib.lse_merge(10, 2, 6, fake, fake, fake, fake, fake, 0, fake, None) == BA_EINVAL  # d/4 must divide 64
     assert lib.lse_merge(10, 2, 64, fake, fake, fake, fake, fake, 7, fake, None) == BA_EINVAL  # bad dtype
+
+
+def test_ring_step_rejects_bad_windows_without_touching_the_gpu():
+    """ba_ring_step_fwd: bf16 plans only; 0 <= win_lo <= win_hi <= N; checks come first."""
+    lib = sda.lib
+    fake = 1 << 40  # never dereferenced
+    pf = Plan.from_workload(W.get("tiny_f32"))
+    assert lib.ba_ring_step_fwd(pf.handle, fake, fake, fake, fake, 0, 8, fake, fake, fake,
+                                pf.workspace_bytes(2), None) == sda.BA_EUNSUPPORTED
+    w = W.get("qwen3_8b_16k_div16")
+    p = Plan.from_workload(w)
+    ws = p.workspace_bytes(2)
+    for lo, hi in ((-1, 5), (10, 5), (w.N - 3, w.N + 1)):
+        assert lib.ba_ring_step_fwd(p.handle, fake, fake, fake, fake, lo, hi, fake, fake, fake, ws, None) == BA_EINVAL
+    assert lib.ba_ring_step_fwd(p.handle, fake, fake, fake, fake, 0, 64, fake, fake, fake, 16, None) == \
+        sda.BA_EWORKSPACE
+    assert lib.ba_ring_step_fwd(p.handle, fake, fake, fake + 2, fake, 0, 64, fake, fake, fake, ws, None) == BA_EINVAL
+    # an empty window is accepted and enqueues nothing (no stream, no device access)
+    assert lib.ba_ring_step_fwd(p.handle, fake, fake, None, None, 5, 5, fake, fake, fake, ws, None) == sda.BA_OK
