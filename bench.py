@@ -126,6 +126,64 @@ def cpu_baseline(w, t, seconds):
             "seconds": el}
 
 
+def hbm_kernels(w, kern):
+    """Branch-local kernels (bf16): algorithmic HBM bytes per launch and the rate
+    against the 8 TB/s peak. Forward, per (branch row, q head): Q 2d, the main
+    partial 4d + 4 in, the merged output 2d + 4 out; per (branch row, kv head):
+    K, V 4d. Backward, per (branch row, q head): Q, dO 4d, the dQ accumulator 4d
+    in, dQ 2d out, LSE and D 8; per (branch row, kv head): K, V in and dK, dV out 8d."""
+    rb, hq, hkv, d = w.Rb, w.num_q_heads, w.num_kv_heads, w.head_dim
+    byt = {"branch_local_fwd": rb * hq * (8 * d + 8) + rb * hkv * 4 * d,
+           "branch_local_bwd": rb * hq * (10 * d + 8) + rb * hkv * 8 * d}
+    out = {}
+    for k, b in byt.items():
+        if k in kern and kern[k][1]:
+            ms = kern[k][0] / kern[k][1]
+            gbs = b / (ms * 1e-3) / 1e9
+            out[k] = {"ms": round(ms, 3), "bytes": b, "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
+
+
+def ring_sim(sda, plan, g, w, stream, kern):
+    """The main-key forward as rank 3 of a CP=8 zigzag ring computes it: the 16
+    chunks arrive in ring order (pair r, 15-r from rank r), each from its own K/V
+    buffer, through ba_ring_step_fwd into one running (O, LSE). Chunks 13-15 lie
+    past the rank's last key and arrive empty. Untimed: the chunk copies and one
+    warmup pass. Compared with the single pass (V transpose + main forward)."""
+    import torch
+    chunk = w.N // 13
+    wins = []
+    for s in range(8):
+        r = (3 - s) % 8
+        for c in (r, 15 - r):
+            wins.append((min(c * chunk, w.N), min((c + 1) * chunk, w.N)))
+    bufs = [(g["k"][lo:hi].clone(), g["v"][lo:hi].clone()) for lo, hi in wins]
+    R = w.Nq + w.Rb
+    o_run = torch.empty((R, w.num_q_heads, w.head_dim), dtype=torch.float32, device=g["q"].device)
+    lse_run = torch.empty((w.num_q_heads, R), dtype=torch.float32, device=g["q"].device)
+    ws = sda.workspace(plan, 2, g["q"].device)
+
+    def run():
+        o_run.zero_()
+        lse_run.fill_(float("-inf"))
+        for (lo, hi), (kw, vw) in zip(wins, bufs):
+            sda.ba_ring_step_fwd(plan, g["q"], g["qb"], kw, vw, lo, hi, o_run, lse_run, ws)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    single = (kern["main_fwd"][0] + kern["vt_transpose"][0]) / max(1, kern["main_fwd"][1])
+    log(f"ring simulation: {len(wins)} windows in {ms:.1f} ms (single pass {single:.1f} ms)")
+    del bufs, o_run, lse_run, ws
+    return {"windows": len(wins), "nonempty": sum(hi > lo for lo, hi in wins), "ms": round(ms, 3),
+            "single_pass_ms": round(single, 3), "ratio": round(ms / single, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +192,8 @@ def main():
     ap.add_argument("--workload", default="ctx256k_rank3")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ring-sim", action="store_true",
+                    help="skip the ring-step simulation measured after the timed steps")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before the warmup, copy a buffer of this many MiB once (a plain copy kernel of known "
                          "size, for scaling hardware byte counters); not part of the timed region")
@@ -246,8 +306,11 @@ def main():
         "roofline": {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
+        "hbm_bound_kernels": hbm_kernels(w, kern),
         "cpu_baseline": None,
     }
+    if not args.no_ring_sim and w.name == "ctx256k_rank3":
+        res["ring_sim"] = ring_sim(sda, plan, g, w, stream, kern)
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on sampled rows for ~{args.cpu_seconds:.0f} s")
         res["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)
