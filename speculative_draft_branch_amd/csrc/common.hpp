@@ -113,6 +113,28 @@ __device__ __forceinline__ int lds_off(int row, int d) {  // element offset of (
   return row * HD + ((((d >> 3) ^ swz<HD>(row))) << 3) + (d & 7);
 }
 
+// LDS DMA (global_load_lds: each lane's BYTES land at lds_dst + lane * BYTES,
+// lds_dst wave-uniform) issued from inline asm, so that the compiler's
+// wait-count tracking does not see it. Seeing one, hipcc treats every later LDS
+// read in the loop as unordered and waits for all LDS reads in flight
+// (lgkmcnt(0)) before the first use of any of them, which turns each operand
+// pipeline into batches. Every reader of DMA'd data waits through dma_barrier
+// (a vmcnt wait and a workgroup barrier, both visible to the compiler); an
+// untracked load only makes the compiler's own vmcnt waits more conservative.
+// The memory clobber keeps every LDS access on its side of the request.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void *src, const void *lds_dst) {
+  static_assert(BYTES == 4 || BYTES == 16, "dword or dwordx4");
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_dst);
+  if constexpr (BYTES == 16)
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0)
+                 : "memory");
+  else
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(src), "{m0}"(m0)
+                 : "memory");
+}
+
 // Padded LDS tiles: each row of HD bf16 followed by 48 unused bytes (19 four-
 // bank groups per row at d = 128, an odd count). Sixteen consecutive rows at
 // the same column then start in sixteen different 4-bank groups, so operand
@@ -136,10 +158,7 @@ __device__ __forceinline__ void stage_padded_async(bf16 *lds, const bf16 *__rest
     const int r = it * NW + w;
     const char *row = reinterpret_cast<const char *>(src + (int64_t)r * HD);
     if (LANES == 64 || lane < LANES)
-      __builtin_amdgcn_global_load_lds(row + lane_off,
-                                       (__attribute__((address_space(3))) void *)(reinterpret_cast<char *>(lds) +
-                                                                                  r * kPadRowBytes<HD>),
-                                       4, 0, 0);
+      lds_dma<4>(row + lane_off, reinterpret_cast<char *>(lds) + r * kPadRowBytes<HD>);
   }
 }
 // Row read (A operand with k = column): lane reads row 32*blk + lane%32,
@@ -276,17 +295,13 @@ struct AsyncTile {
     if (k0 + ROWS - 1 <= last) {
 #pragma unroll
       for (int it = 0; it < PER_WAVE; ++it)
-        __builtin_amdgcn_global_load_lds(tb + off[it],
-                                         (__attribute__((address_space(3))) void *)(lds + (lds_block + it) * 512),
-                                         16, 0, 0);
+        lds_dma<16>(tb + off[it], lds + (lds_block + it) * 512);
     } else {
 #pragma unroll
       for (int it = 0; it < PER_WAVE; ++it) {
         // rows past the end read row `last` instead (callers mask those keys)
         const uint32_t back = (uint32_t)max(k0 + row[it] - last, 0) * (uint32_t)row_stride * 2u;
-        __builtin_amdgcn_global_load_lds(tb + (off[it] - back),
-                                         (__attribute__((address_space(3))) void *)(lds + (lds_block + it) * 512),
-                                         16, 0, 0);
+        lds_dma<16>(tb + (off[it] - back), lds + (lds_block + it) * 512);
       }
     }
   }
@@ -303,9 +318,7 @@ struct AsyncTile {
     for (int it = 0; it < PER_WAVE; ++it) {
       const int r = min(max(k0 + row[it], first), last);
       const uint32_t chunk = off[it] - (uint32_t)(row[it] * row_stride) * 2u;  // byte offset within the row
-      __builtin_amdgcn_global_load_lds(b + (int64_t)r * row_stride * 2 + chunk,
-                                       (__attribute__((address_space(3))) void *)(lds + (lds_block + it) * 512),
-                                       16, 0, 0);
+      lds_dma<16>(b + (int64_t)r * row_stride * 2 + chunk, lds + (lds_block + it) * 512);
     }
   }
 };
@@ -324,9 +337,7 @@ template <int N>
 __device__ __forceinline__ void stage_words_async(void *lds, const void *__restrict__ src, int lane) {
 #pragma unroll
   for (int it = 0; it < N; ++it)
-    __builtin_amdgcn_global_load_lds(static_cast<const uint32_t *>(src) + it * 64 + lane,
-                                     (__attribute__((address_space(3))) void *)(static_cast<uint32_t *>(lds) + it * 64),
-                                     4, 0, 0);
+    lds_dma<4>(static_cast<const uint32_t *>(src) + it * 64 + lane, static_cast<uint32_t *>(lds) + it * 64);
 }
 
 // Workgroup barrier after this wave's LDS reads and all but its VM most recent
