@@ -63,6 +63,7 @@ __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const b
       return *reinterpret_cast<const bf16x8 *>(((i & 1) ? sV : sK) + off);
     };
     bf16x8 ring[kDqRing];
+    __builtin_amdgcn_s_setprio(1);  // a wave in an MFMA stretch wins issue; the other wave's VALU fills in
 #pragma unroll
     for (int i = 0; i < kDqRing; ++i) ring[i] = rd(i);
     __builtin_amdgcn_sched_barrier(0);
@@ -73,6 +74,7 @@ __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const b
       if (i + kDqRing < 2 * KS) ring[i % kDqRing] = rd(i + kDqRing);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     bf16x8 db[2];  // dS^T operands of the block's two 16-key k-steps
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -84,6 +86,7 @@ __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const b
       db[i >> 3][i & 7] = (bf16)(p * (dp[i] - st.dd));
     }
     // dQ^T += K^T dS^T; slot 8*half + 4c + j <-> key 16kk + 8c + 4*half + j.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       const int kk = kb * 2 + h2;
@@ -95,6 +98,7 @@ __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const b
         st.acc[dt] = mfma32(a, db[h2], st.acc[dt]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 }
 
@@ -336,6 +340,7 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
         sc[b] = f32x16{};
         dp[b] = f32x16{};
       }
+      __builtin_amdgcn_s_setprio(1);  // a wave in an MFMA stretch wins issue; the other wave's VALU fills in
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 aq = pad_row_read<HD>(sQ, st.r_base, rb, ks);
@@ -346,6 +351,7 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
           dp[b] = mfma32(ao, st.vf[b][ks], dp[b]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int r0 = rb * 32 + i4 * 8 + 4 * (lane >> 5);
@@ -368,6 +374,7 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
     }
     // dV += P^T dO, dK += dS^T Q over these 32 rows (two 16-row k-steps).
     // Operand slot 8*half + 4c + j <-> row 32rb + 16kh + 8c + 4*half + j.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
@@ -382,6 +389,7 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 }
 
@@ -432,14 +440,17 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void main_bwd_dkdv_bf16_kernel(Met
   const KTile kt = load_ktile(mt.ktiles + uni(mt.bwd_order[blockIdx.x / hkv]));
   const float sl2 = mt.scale * kLog2e;
 
-  // Query tile qi, kv head g -> one LDS buffer (all asynchronous).
+  // Query tile qi, kv head g -> one LDS buffer (all asynchronous). The row
+  // metadata goes first: an address the compiler keeps in scratch is reloaded
+  // there, and waiting for that reload waits (in order) for every load issued
+  // before it, which would otherwise include this tile's Q and dO rows.
   auto prefetch = [&](int qi, bf16 *sQ, bf16 *sO, float *sL, float *sD, int *sE) {
     const int64_t tb = ((int64_t)qi * hkv + g) * BM;
-    stage_padded_async<HD, BM, NT / 64>(sQ, qt_rows + tb * HD, wave, lane);
-    stage_padded_async<HD, BM, NT / 64>(sO, do_rows + tb * HD, wave, lane);
     if (wave == 0) stage_words_async<BM / 64>(sL, lt + tb, lane);
     else if (wave == 1) stage_words_async<BM / 64>(sD, dtt + tb, lane);
     else if (wave == 2) stage_words_async<kTileMetaWords / 64>(sE, et + (int64_t)qi * kTileMetaWords, lane);
+    stage_padded_async<HD, BM, NT / 64>(sQ, qt_rows + tb * HD, wave, lane);
+    stage_padded_async<HD, BM, NT / 64>(sO, do_rows + tb * HD, wave, lane);
   };
   if (kt.qt_begin < kt.qt_end) prefetch(kt.qt_begin, sQ0, sO0, sL0, sD0, sE0);
 
