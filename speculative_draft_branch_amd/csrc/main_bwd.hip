@@ -220,7 +220,8 @@ __global__ __launch_bounds__(256, 2) void main_bwd_dq_bf16_kernel(Meta mt, const
 // ---------------------------------------------------------------------------
 // Backward preprocess for the bf16 path, one workgroup per (query tile, kv
 // head): the tile's 128 MFMA rows in order -- Q and dO rows, LSE * log2(e),
-// D = rowsum(dO * O) -- plus (kv head 0) each row's prefix end, so the
+// -D with D = rowsum(dO * O) (the start value of the dK/dV kernel's dP
+// accumulator) -- plus (kv head 0) each row's prefix end, so the
 // key-tile-major kernel streams contiguous 32 KB blocks. Also writes D in the
 // [Hq, rows] layout for the dq and branch-local kernels. Every (row, q head)
 // lies in exactly one (query tile, kv head).
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(256) void bwd_gather_bf16_kernel(Meta mt, const bf1
     if (ok) {
       const float l = is_main ? lse[(int64_t)h * mt.Nq + row] : lseb[(int64_t)h * mt.Rb + (row - mt.Nq)];
       lt[trow] = l * kLog2e;
-      dtt[trow] = dsum;
+      dtt[trow] = -dsum;
       delta[(int64_t)h * (mt.Nq + mt.Rb) + row] = dsum;
     } else {
       lt[trow] = INFINITY;
@@ -333,12 +334,20 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
     bf16x8 pa[KB][2], dsa[KB][2];
     {
       // S and dP of these rows, then P and dS element by element from the fp32
-      // values (P rounded to bf16 once, for the dV product).
+      // values (P rounded to bf16 once, for the dV product). The dP accumulator
+      // starts at -D of its rows (staged per tile), so the MFMAs deliver dP - D.
       f32x16 sc[KB], dp[KB];
+      f32x16 nd;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(sD + rb * 32 + i4 * 8 + 4 * (lane >> 5));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nd[i4 * 4 + e] = x[e];
+      }
 #pragma unroll
       for (int b = 0; b < KB; ++b) {
         sc[b] = f32x16{};
-        dp[b] = f32x16{};
+        dp[b] = nd;
       }
       __builtin_amdgcn_s_setprio(1);  // a wave in an MFMA stretch wins issue; the other wave's VALU fills in
 #pragma unroll
@@ -356,7 +365,6 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
       for (int i4 = 0; i4 < 4; ++i4) {
         const int r0 = rb * 32 + i4 * 8 + 4 * (lane >> 5);
         const f32x4 l2 = *reinterpret_cast<const f32x4 *>(sL2 + r0);
-        const f32x4 dd = *reinterpret_cast<const f32x4 *>(sD + r0);
         int4 ends = {0, 0, 0, 0};
         if constexpr (MASK) ends = *reinterpret_cast<const int4 *>(sEnd + r0);
 #pragma unroll
@@ -367,7 +375,7 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
             float p = fast_exp2(fmaf(sc[b][i], sl2, -l2[e]));
             if (MASK && (ends[e] < st.my_key[b] || st.my_key[b] >= st.key_hi)) p = 0.0f;
             pa[b][i >> 3][i & 7] = (bf16)p;
-            dsa[b][i >> 3][i & 7] = (bf16)(p * (dp[b][i] - dd[e]));
+            dsa[b][i >> 3][i & 7] = (bf16)(p * dp[b][i]);
           }
         }
       }
