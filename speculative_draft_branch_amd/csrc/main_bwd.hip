@@ -35,7 +35,8 @@ struct DqState {
   static constexpr int DT = HD / 32;
   bf16x8 qf[KS], of[KS];
   f32x16 acc[DT];
-  float l2, dd;
+  float l2;
+  f32x16 nd;  // -D of the lane's row in every element: the start value of dP^T
   int end, wmin;
   int grp, in_j, in_q, lane;
 };
@@ -69,7 +70,7 @@ __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const b
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i) {
-      if (i & 1) dp = mfma32(ring[i % kDqRing], st.of[i >> 1], dp);
+      if (i & 1) dp = mfma32(ring[i % kDqRing], st.of[i >> 1], i == 1 ? st.nd : dp);
       else s = mfma32(ring[i % kDqRing], st.qf[i >> 1], s);
       if (i + kDqRing < 2 * KS) ring[i % kDqRing] = rd(i + kDqRing);
       __builtin_amdgcn_sched_barrier(0);
@@ -83,7 +84,7 @@ __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const b
         const int key = k0 + kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
         if (key > st.end) p = 0.0f;
       }
-      db[i >> 3][i & 7] = (bf16)(p * (dp[i] - st.dd));
+      db[i >> 3][i & 7] = (bf16)(p * dp[i]);
     }
     // dQ^T += K^T dS^T; slot 8*half + 4c + j <-> key 16kk + 8c + 4*half + j.
     __builtin_amdgcn_s_setprio(1);
@@ -166,11 +167,13 @@ __global__ __launch_bounds__(256, 2) void main_bwd_dq_bf16_kernel(Meta mt, const
     }
   }
   st.l2 = INFINITY;  // padding rows: P = 0
-  st.dd = 0.0f;
+  float dd = 0.0f;
   if (row >= 0) {
     st.l2 = (is_main ? lse[(int64_t)h * mt.Nq + row] : lseb[(int64_t)h * mt.Rb + (row - mt.Nq)]) * kLog2e;
-    st.dd = delta[(int64_t)h * R + row];
+    dd = delta[(int64_t)h * R + row];
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) st.nd[i] = -dd;
   st.wmin = wave_min(row >= 0 ? st.end : INT_MAX);
   const int wmax = wave_max(st.end);
   const float sl2 = mt.scale * kLog2e;
