@@ -27,11 +27,70 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3  # published fp32 vector peak
+CLOCK_PEAK_MHZ = 2400.0  # the clock the peaks are quoted at
 METRIC = "branch-attention fwd+bwd TFLOP/s and % bf16 MFMA peak, 256K-ctx 1-GPU share"
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class ClockSampler:
+    """Shader clock during the timed steps: a thread polls `amd-smi metric
+    --clock --json` (the current gfx clock of every XCD) and keeps the mean of
+    the clocks that are active (above 1 GHz). None when the tool is missing or
+    its output cannot be read."""
+
+    def __init__(self):
+        import shutil
+        import threading
+        self.tool = shutil.which("amd-smi")
+        self.samples = []
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        import subprocess
+        r = subprocess.run([self.tool, "metric", "--clock", "--json"], capture_output=True, text=True, timeout=20)
+        data = json.loads(r.stdout)
+        clks = []
+
+        def walk(x):
+            if isinstance(x, dict):
+                for k, v in x.items():
+                    if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict):
+                        val = v["clk"].get("value")
+                        if isinstance(val, (int, float)):
+                            clks.append(float(val))
+                    else:
+                        walk(v)
+            elif isinstance(x, list):
+                for v in x:
+                    walk(v)
+        walk(data)
+        return [c for c in clks if c > 1000.0]
+
+    def _run(self):
+        while not self.stop.is_set():
+            try:
+                self.samples.extend(self._read())
+            except Exception:
+                return
+            self.stop.wait(0.2)
+
+    def __enter__(self):
+        if self.tool:
+            self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        if self.thread.is_alive():
+            self.thread.join(timeout=30)
+
+    def mhz(self):
+        return round(sum(self.samples) / len(self.samples), 1) if self.samples else None
 
 
 def kernel_source_hash(names):
@@ -216,7 +275,10 @@ def main():
     t_gen = time.time()
     t = make_inputs(w, grads=True)
     log(f"inputs generated in {time.time() - t_gen:.1f} s")
-    g = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() for k, v in t.items()}
+    if w.dtype == "bf16":
+        g = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() for k, v in t.items()}
+    else:
+        g = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in t.items()}
     t_plan = time.time()
     plan = sda.Plan.from_workload(w)
     log(f"plan built in {time.time() - t_plan:.2f} s: {plan.n_qtiles} query tiles, {plan.n_ktiles} key tiles")
@@ -252,12 +314,14 @@ def main():
     sda.timing_enable(True)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
+    with ClockSampler() as clk:
+        e0.record(stream)
+        for i in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
     sda.timing_enable(False)
+    clock_mhz = clk.mhz()
     ms = e0.elapsed_time(e1) / args.steps
     kern = sda.timing_read()
     log(f"timed {args.steps} steps: {ms:.1f} ms/step")
@@ -274,6 +338,10 @@ def main():
     # QK^T, dO V^T, P^T dO, dS^T Q (8d)
     algo = {"main_fwd": 4 * d * hq * main_pairs, "main_bwd_dq": 6 * d * hq * main_pairs,
             "main_bwd_dkdv": 8 * d * hq * main_pairs}
+    peak, bound = PEAK_BF16_TFLOPS, "mfma"
+    if w.dtype != "bf16":  # float32: plain vector kernels, one backward kernel does dQ, dK and dV (10d)
+        algo = {"main_fwd": 4 * d * hq * main_pairs, "main_bwd_dkdv": 10 * d * hq * main_pairs}
+        peak, bound = PEAK_FP32_TFLOPS, "alu"
     dominant = max(algo, key=lambda k: kern[k][0])
     dom_ms = kern[dominant][0] / max(1, kern[dominant][1])
     achieved = algo[dominant] / (dom_ms * 1e-3) / 1e12
@@ -290,7 +358,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "tokens_total": 16 * 16384 if w.name == "ctx256k_rank3" else w.N,
                    "main_keys": w.N, "main_query_rows": w.Nq, "branch_rows": w.Rb,
@@ -301,12 +369,16 @@ def main():
         "bwd_ms": round(bwd_ms, 3),
         "fwd_tflops": round(flops_fwd / (fwd_ms * 1e-3) / 1e12, 2),
         "bwd_tflops": round(flops_bwd / (bwd_ms * 1e-3) / 1e12, 2),
-        "main_fwd_frac_peak": round(4 * d * hq * main_pairs / (fwd_main_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "main_fwd_frac_peak": round(4 * d * hq * main_pairs / (fwd_main_ms * 1e-3) / 1e12 / peak, 4),
         "kernels_ms_per_launch": {k: round(v[0] / max(1, v[1]), 3) for k, v in kern.items() if v[1]},
-        "roofline": {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": bound, "kernel": dominant, "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic},
-        "hbm_bound_kernels": hbm_kernels(w, kern),
+        # shader clock while the steps ran, and the dominant kernel's fraction of
+        # the peak scaled to that clock (the peak assumes 2.4 GHz)
+        "clock_mhz": clock_mhz,
+        "frac_at_clock": (round(achieved / (peak * clock_mhz / CLOCK_PEAK_MHZ), 4) if clock_mhz else None),
+        "hbm_bound_kernels": hbm_kernels(w, kern) if w.dtype == "bf16" else None,
         "cpu_baseline": None,
     }
     if not args.no_ring_sim and w.name == "ctx256k_rank3":
