@@ -222,9 +222,11 @@ __global__ __launch_bounds__(256, 2) void main_bwd_dq_bf16_kernel(Meta mt, const
 
 // ---------------------------------------------------------------------------
 // Backward preprocess for the bf16 path, one workgroup per (query tile, kv
-// head): the tile's 128 MFMA rows in order -- Q and dO rows, LSE * log2(e),
-// -D with D = rowsum(dO * O) (the start value of the dK/dV kernel's dP
-// accumulator) -- plus (kv head 0) each row's prefix end, so the
+// head): the tile's 128 MFMA rows in order -- Q rows multiplied by
+// scale * log2(e) (rounded to bf16), dO rows, -LSE * log2(e) and -D with
+// D = rowsum(dO * O) (the start values of the dK/dV kernel's S and dP
+// accumulators, so its MFMAs deliver the exponent of P and dP - D directly)
+// -- plus (kv head 0) each row's prefix end, so the
 // key-tile-major kernel streams contiguous 32 KB blocks. Also writes D in the
 // [Hq, rows] layout for the dq and branch-local kernels. Every (row, q head)
 // lies in exactly one (query tile, kv head).
@@ -262,10 +264,15 @@ __global__ __launch_bounds__(256) void bwd_gather_bf16_kernel(Meta mt, const bf1
     const uint4 *qs = reinterpret_cast<const uint4 *>((is_main ? q : qb) + off);
     const uint4 *ds = reinterpret_cast<const uint4 *>((is_main ? d_o : d_ob) + off);
     const uint4 *os = reinterpret_cast<const uint4 *>((is_main ? o : ob) + off);
+    const float sl2 = mt.scale * kLog2e;
 #pragma unroll
     for (int c = 0; c < NCH / 2; ++c) {
       const int ch = half * (NCH / 2) + c;
-      qd[ch] = qs[ch];
+      const bf16x8 xb = __builtin_bit_cast(bf16x8, qs[ch]);
+      bf16x8 sq;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq[e] = (bf16)((float)xb[e] * sl2);
+      qd[ch] = __builtin_bit_cast(uint4, sq);
       const uint4 y = ds[ch];
       od[ch] = y;
       const bf16x8 yb = __builtin_bit_cast(bf16x8, y);
@@ -285,11 +292,11 @@ __global__ __launch_bounds__(256) void bwd_gather_bf16_kernel(Meta mt, const bf1
   if (half == 0) {
     if (ok) {
       const float l = is_main ? lse[(int64_t)h * mt.Nq + row] : lseb[(int64_t)h * mt.Rb + (row - mt.Nq)];
-      lt[trow] = l * kLog2e;
+      lt[trow] = -l * kLog2e;
       dtt[trow] = -dsum;
       delta[(int64_t)h * (mt.Nq + mt.Rb) + row] = dsum;
     } else {
-      lt[trow] = INFINITY;
+      lt[trow] = -INFINITY;  // padding rows: P = 0
       dtt[trow] = 0.0f;
     }
     if (g == 0) et[(int64_t)qi * kTileMetaWords + m] = ok ? mt.tile_row_end[tile.row_begin + bi] : -1;
@@ -339,17 +346,24 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
       // S and dP of these rows, then P and dS element by element from the fp32
       // values (P rounded to bf16 once, for the dV product). The dP accumulator
       // starts at -D of its rows (staged per tile), so the MFMAs deliver dP - D.
+      // Likewise S starts at -LSE * log2(e) of its rows and Q is staged scaled
+      // by scale * log2(e), so the S MFMAs deliver the exponent of P.
       f32x16 sc[KB], dp[KB];
-      f32x16 nd;
+      f32x16 nd, nl;
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(sD + rb * 32 + i4 * 8 + 4 * (lane >> 5));
+        const int r0 = rb * 32 + i4 * 8 + 4 * (lane >> 5);
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(sD + r0);
+        const f32x4 y = *reinterpret_cast<const f32x4 *>(sL2 + r0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) nd[i4 * 4 + e] = x[e];
+        for (int e = 0; e < 4; ++e) {
+          nd[i4 * 4 + e] = x[e];
+          nl[i4 * 4 + e] = y[e];
+        }
       }
 #pragma unroll
       for (int b = 0; b < KB; ++b) {
-        sc[b] = f32x16{};
+        sc[b] = nl;
         dp[b] = nd;
       }
       __builtin_amdgcn_s_setprio(1);  // a wave in an MFMA stretch wins issue; the other wave's VALU fills in
@@ -367,7 +381,6 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int r0 = rb * 32 + i4 * 8 + 4 * (lane >> 5);
-        const f32x4 l2 = *reinterpret_cast<const f32x4 *>(sL2 + r0);
         int4 ends = {0, 0, 0, 0};
         if constexpr (MASK) ends = *reinterpret_cast<const int4 *>(sEnd + r0);
 #pragma unroll
@@ -375,7 +388,7 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
           const int i = i4 * 4 + e;
 #pragma unroll
           for (int b = 0; b < KB; ++b) {
-            float p = fast_exp2(fmaf(sc[b][i], sl2, -l2[e]));
+            float p = fast_exp2(sc[b][i]);
             if (MASK && (ends[e] < st.my_key[b] || st.my_key[b] >= st.key_hi)) p = 0.0f;
             pa[b][i >> 3][i & 7] = (bf16)p;
             dsa[b][i >> 3][i & 7] = (bf16)(p * dp[b][i]);
@@ -505,7 +518,8 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void main_bwd_dkdv_bf16_kernel(Met
   }
 
   // dK, dV of the wave's keys: element i of block (b, dt) is key wkey_lo +
-  // 32b + (i/4)*8 + 4*(lane/32) + i%4, d = 32dt + lane%32.
+  // 32b + (i/4)*8 + 4*(lane/32) + i%4, d = 32dt + lane%32. The staged Q rows
+  // carry scale * log2(e), so dK = scale * dS^T Q = ln(2) * dS^T Q_staged.
 #pragma unroll
   for (int b = 0; b < KB; ++b)
 #pragma unroll
@@ -515,7 +529,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void main_bwd_dkdv_bf16_kernel(Met
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const int64_t dst = ((int64_t)key * hkv + g) * HD + dt * 32 + (lane & 31);
-          dk[dst] = (bf16)(mt.scale * st.adk[b][dt][i]);
+          dk[dst] = (bf16)(kLn2 * st.adk[b][dt][i]);
           dv[dst] = (bf16)st.adv[b][dt][i];
         }
       }
