@@ -43,6 +43,8 @@ struct DqState {
 
 // One 64-key tile [k0, k0 + 64) of the wave's 32 rows against LDS tiles sK, sV.
 constexpr int kDqRing = 4;
+// K^T operands in flight in the dQ product pipeline.
+constexpr int kDqKRing = 4;
 
 // MASK: some key of the tile lies past some row's prefix end (a wave-uniform
 // condition, so the unmasked tiles carry no per-element selects).
@@ -76,6 +78,15 @@ __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const b
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
+    // dQ^T += K^T dS^T in 2*DT steps n = (h2, dt), K^T through the transposing
+    // LDS read; slot 8*half + 4c + j <-> key 16kk + 8c + 4*half + j. Operands are
+    // requested kDqKRing steps ahead of their MFMA.
+    auto rdk = [&](int n) {
+      const int kk = kb * 2 + n / DT, dt = n % DT;
+      const int key0 = kk * 16 + 4 * (st.grp >> 1) + st.in_j;
+      const int d = dt * 32 + (st.grp & 1) * 16 + 4 * st.in_q;
+      return join(lds_read_tr(sK + lds_off<HD>(key0, d)), lds_read_tr(sK + lds_off<HD>(key0 + 8, d)));
+    };
     bf16x8 db[2];  // dS^T operands of the block's two 16-key k-steps
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -86,18 +97,16 @@ __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const b
       }
       db[i >> 3][i & 7] = (bf16)(p * dp[i]);
     }
-    // dQ^T += K^T dS^T; slot 8*half + 4c + j <-> key 16kk + 8c + 4*half + j.
+    bf16x8 kr[kDqKRing];
+#pragma unroll
+    for (int i = 0; i < kDqKRing; ++i) kr[i] = rdk(i);
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int kk = kb * 2 + h2;
-      const int key0 = kk * 16 + 4 * (st.grp >> 1) + st.in_j;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = dt * 32 + (st.grp & 1) * 16 + 4 * st.in_q;
-        const bf16x8 a = join(lds_read_tr(sK + lds_off<HD>(key0, d)), lds_read_tr(sK + lds_off<HD>(key0 + 8, d)));
-        st.acc[dt] = mfma32(a, db[h2], st.acc[dt]);
-      }
+    for (int n = 0; n < 2 * DT; ++n) {
+      st.acc[n % DT] = mfma32(kr[n % kDqKRing], db[n / DT], st.acc[n % DT]);
+      if (n + kDqKRing < 2 * DT) kr[n % kDqKRing] = rdk(n + kDqKRing);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
   }
@@ -333,7 +342,7 @@ struct DkdvState {
 // row's prefix end or the key range cuts through the wave's keys.
 template <int HD, int KB, bool MASK>
 __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ, const bf16 *sdO, const float *sL2,
-                                          const float *sD, const int *sEnd, float sl2) {
+                                          const float *sD, const int *sEnd) {
   constexpr int BM = kTileRows;
   constexpr int KS = DkdvState<HD, KB>::KS, DT = DkdvState<HD, KB>::DT;
 #pragma unroll 1
@@ -420,15 +429,15 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
 // One query tile (128 MFMA rows staged in LDS) against the wave's 32*KB keys.
 template <int HD, int KB>
 __device__ __forceinline__ void dkdv_tile(DkdvState<HD, KB> &st, const bf16 *sQ, const bf16 *sdO, const float *sL2,
-                                          const float *sD, const int *sEnd, float sl2) {
+                                          const float *sD, const int *sEnd) {
   constexpr int BM = kTileRows;
   constexpr int WK = 32 * KB;  // keys of this wave
   const int end_min = uni(sEnd[BM]), end_max = uni(sEnd[BM + 1]), valid_rows = uni(sEnd[BM + 2]);
   if (end_max < st.wkey_lo || st.wkey_lo >= st.key_hi) return;  // no row of this tile sees the wave's keys
   if (end_min < st.wkey_lo + WK - 1 || st.wkey_lo + WK - 1 >= st.key_hi || valid_rows < BM)
-    dkdv_rows<HD, KB, true>(st, sQ, sdO, sL2, sD, sEnd, sl2);
+    dkdv_rows<HD, KB, true>(st, sQ, sdO, sL2, sD, sEnd);
   else
-    dkdv_rows<HD, KB, false>(st, sQ, sdO, sL2, sD, sEnd, sl2);
+    dkdv_rows<HD, KB, false>(st, sQ, sdO, sL2, sD, sEnd);
 }
 
 }  // namespace
@@ -462,7 +471,6 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void main_bwd_dkdv_bf16_kernel(Met
   const int hkv = mt.hkv;
   const int g = blockIdx.x % hkv;
   const KTile kt = load_ktile(mt.ktiles + uni(mt.bwd_order[blockIdx.x / hkv]));
-  const float sl2 = mt.scale * kLog2e;
 
   // Query tile qi, kv head g -> one LDS buffer (all asynchronous). The row
   // metadata goes first: an address the compiler keeps in scratch is reloaded
@@ -510,11 +518,11 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void main_bwd_dkdv_bf16_kernel(Met
   for (int qi = kt.qt_begin; qi < kt.qt_end; qi += 2) {
     dma_barrier<0>();  // tile qi is in buffer 0; every wave is done with buffer 1
     if (qi + 1 < kt.qt_end) prefetch(qi + 1, sQ1, sO1, sL1, sD1, sE1);
-    dkdv_tile<HD, KB>(st, sQ0, sO0, sL0, sD0, sE0, sl2);
+    dkdv_tile<HD, KB>(st, sQ0, sO0, sL0, sD0, sE0);
     if (qi + 1 >= kt.qt_end) break;
     dma_barrier<0>();  // tile qi+1 is in buffer 1; every wave is done with buffer 0
     if (qi + 2 < kt.qt_end) prefetch(qi + 2, sQ0, sO0, sL0, sD0, sE0);
-    dkdv_tile<HD, KB>(st, sQ1, sO1, sL1, sD1, sE1, sl2);
+    dkdv_tile<HD, KB>(st, sQ1, sO1, sL1, sD1, sE1);
   }
 
   // dK, dV of the wave's keys: element i of block (b, dt) is key wkey_lo +
