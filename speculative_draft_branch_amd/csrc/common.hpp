@@ -343,12 +343,11 @@ __device__ __forceinline__ void stage_words_async(void *lds, const void *__restr
 // Workgroup barrier after this wave's LDS reads and all but its VM most recent
 // vector-memory requests (LDS DMA among them) have completed: every tile
 // requested before those is in LDS for every wave after the barrier, and no
-// LDS read of the phase before it is still in flight. The wait goes through the
-// builtin so the compiler's own wait insertion sees it: with a wait it cannot
-// see, it assumes a DMA into a buffer may still be pending when the buffer is
-// next read and waits for every load in flight, including DMA just issued for
-// later tiles. The empty asm statements stop the compiler moving memory
-// accesses across. VM = 63 waits for LDS reads only.
+// LDS read of the phase before it is still in flight. This barrier is the only
+// wait for DMA'd data (lds_dma hides the DMA from the compiler's tracking); the
+// wait goes through the builtin so the compiler's own wait insertion sees it.
+// The empty asm statements stop the compiler moving memory accesses across.
+// VM = 63 waits for LDS reads only.
 template <int VM>
 __device__ __forceinline__ void dma_barrier() {
   static_assert(VM >= 0 && VM <= 63, "vmcnt field");

@@ -127,8 +127,7 @@ __global__ __launch_bounds__(256, 2) void main_bwd_dq_bf16_kernel(Meta mt, const
                                                                float *__restrict__ dq_acc) {
   constexpr int BN = 64;
   constexpr int KS = HD / 16, DT = HD / 32;
-  // K and V of one buffer share an array (one address for both reads); the
-  // two buffers stay distinct objects for the compiler's DMA wait tracking.
+  // K and V of one buffer share an array (one address for both reads).
   __shared__ __attribute__((aligned(16))) bf16 sKV0[2 * BN * HD];
   __shared__ __attribute__((aligned(16))) bf16 sKV1[2 * BN * HD];
   bf16 *const sK0 = sKV0, *const sV0 = sKV0 + BN * HD;
@@ -456,9 +455,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void main_bwd_dkdv_bf16_kernel(Met
   constexpr int KS = HD / 16, DT = HD / 32;
   static_assert(kBwdKeys == 32 * KB * (NT / 64) && BM == 128, "tile shape");
   // Padded tiles (see stage_padded_async). Q and dO of one buffer share an
-  // array, so a read of either is one address plus a constant offset; the two
-  // buffers stay distinct objects, which lets the compiler see that reads of
-  // one never wait for DMA into the other.
+  // array, so a read of either is one address plus a constant offset.
   constexpr int TILE = BM * kPadRowBytes<HD> / 2;  // elements per padded tile
   __shared__ __attribute__((aligned(16))) bf16 sQO0[2 * TILE];
   __shared__ __attribute__((aligned(16))) bf16 sQO1[2 * TILE];

@@ -282,7 +282,7 @@ __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf
   // the softmax of tile (u-1)/2. Tile j's K is in buffer j%2 from slot 2j, its
   // V in buffer j%2 from slot 2j+2; both are requested at slot 2j-2 and 2j
   // respectively, so every DMA has two phases to land. The loop is unrolled
-  // over the tile parity so each buffer is a distinct LDS object.
+  // over the tile parity, so every buffer address is a constant.
   f32x16 s[2];
   bf16x8 pb[4];
   const int nslots = 2 * ntiles + 2;
