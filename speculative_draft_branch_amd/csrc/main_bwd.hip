@@ -10,15 +10,18 @@
 // Two kernels, no atomics:
 //  * dq: query-tile major, the forward's work unit (query tile x its key range,
 //    64-key LDS tiles). S^T = K Q^T and dP^T = V dO^T put one query row on each
-//    lane; dQ^T += K^T dS^T takes K through the transposing LDS read and dS^T
-//    straight from registers. dQ is written once per row (float32, into the
-//    accumulator the branch-local backward adds to).
-//  * dkdv: key-tile major: 256 main keys of one kv head (four waves of 64
+//    lane (dP^T starts from -D of that row); dQ^T += K^T dS^T takes K through
+//    the transposing LDS read and dS^T straight from registers. dQ is written
+//    once per row (float32, into the accumulator the branch-local backward adds
+//    to).
+//  * dkdv: key-tile major: 256 main keys of one kv head (eight waves of 32
 //    keys, sharing every staged query tile) against every query tile whose rows
-//    may see them; each wave owns 64 keys and keeps their dK, dV
-//    in registers across all query tiles, written once, summed over the group's
-//    q heads. S = Q K^T puts the key on the lane, so P and dS are directly the
-//    A operands of dV += P^T dO and dK += dS^T Q (dO and Q via the transposing
+//    may see them; each wave keeps its keys' dK, dV in registers across all
+//    query tiles, written once, summed over the group's q heads. The gather
+//    stages Q scaled by scale * log2(e) and -LSE * log2(e), -D per row, so the
+//    S and dP MFMAs (started from those) deliver the exponent of P and dP - D.
+//    S = Q K^T puts the key on the lane, so P and dS are directly the A
+//    operands of dV += P^T dO and dK += dS^T Q (dO and Q via the transposing
 //    LDS read).
 #include <climits>
 
