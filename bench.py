@@ -94,10 +94,15 @@ class ClockSampler:
 
 
 def kernel_source_hash(names):
+    """Hash of the code of the kernel's sources: line comments, trailing blanks
+    and empty lines are left out, so an edit of comments alone keeps it."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "speculative_draft_branch_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "speculative_draft_branch_amd", "csrc", n)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update((code + "\n").encode())
     return h.hexdigest()[:16]
 
 
