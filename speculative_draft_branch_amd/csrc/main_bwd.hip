@@ -118,7 +118,7 @@ __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const b
 }  // namespace
 
 template <int HD>
-__global__ __launch_bounds__(256, 2) void main_bwd_dq_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
+__global__ __launch_bounds__(512, 1) void main_bwd_dq_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
                                                                const bf16 *__restrict__ qb,
                                                                const bf16 *__restrict__ k,
                                                                const bf16 *__restrict__ v,
@@ -136,27 +136,38 @@ __global__ __launch_bounds__(256, 2) void main_bwd_dq_bf16_kernel(Meta mt, const
   bf16 *const sK0 = sKV0, *const sV0 = sKV0 + BN * HD;
   bf16 *const sK1 = sKV1, *const sV1 = sKV1 + BN * HD;
 
+  // Work unit: the forward's pair of adjacent query tiles of one sequence
+  // (waves 0-3 the first, 4-7 the second) against the union of their key
+  // ranges; every K/V tile in LDS serves both, which halves the K/V streams an
+  // XCD's L2 has to hold.
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hkv = mt.hkv, G = mt.G;
   const int g = blockIdx.x % hkv;
-  const QTile tile = load_qtile(mt.qtiles + uni(mt.fwd_order[blockIdx.x / hkv]));
+  const int pair = blockIdx.x / hkv;
+  const int ta = uni(mt.fwd_pairs[2 * pair]), tb = uni(mt.fwd_pairs[2 * pair + 1]);
+  const QTile tile_a = load_qtile(mt.qtiles + ta);
+  const int end_b = tb >= 0 ? uni(mt.qtiles[tb].end_max) : -1;
   const int64_t R = mt.Nq + mt.Rb;
-  const int kv_lo = tile.kv_lo, kv_end = tile.end_max;
+  const int kv_lo = tile_a.kv_lo, kv_end = max(tile_a.end_max, end_b);
   const int ntiles = (kv_end - kv_lo + BN) / BN;
-  AsyncTile<HD, BN, 256> kvt;
+  AsyncTile<HD, BN, 512> kvt;
   kvt.init(hkv * HD, tid);
   const bf16 *kg = k + (int64_t)g * HD, *vg = v + (int64_t)g * HD;
   kvt.load(sK0, kg, kv_lo, kv_end);
   kvt.load(sV0, vg, kv_lo, kv_end);
 
   DqState<HD> st;
-  const int mrow = wave * 32 + (lane & 31);
+  const int mrow = (wave & 3) * 32 + (lane & 31);
   const int bi = mrow / G, hj = mrow - bi * G;
   int row = -1;
   st.end = -1;
-  if (bi < tile.nrows) {
-    row = mt.tile_row_id[tile.row_begin + bi];
-    st.end = mt.tile_row_end[tile.row_begin + bi];
+  const int my_tile = (wave >> 2) ? tb : ta;
+  if (my_tile >= 0) {
+    const QTile tile = load_qtile(mt.qtiles + my_tile);
+    if (bi < tile.nrows) {
+      row = mt.tile_row_id[tile.row_begin + bi];
+      st.end = mt.tile_row_end[tile.row_begin + bi];
+    }
   }
   const int h = mt.group_heads[g * G + hj];
   const bool is_main = row >= 0 && row < mt.Nq;
@@ -561,12 +572,12 @@ hipError_t launch_bwd_gather_bf16(const Meta &mt, const bf16 *q, const bf16 *qb,
 hipError_t launch_main_bwd_dq_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *v,
                                    const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
                                    const float *delta, float *dq_acc, hipStream_t st) {
-  if (mt.n_qtiles == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((int64_t)mt.n_qtiles * mt.hkv);
+  if (mt.n_fwd_pairs == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv);
   if (mt.d == 128)
-    main_bwd_dq_bf16_kernel<128><<<grid, 256, 0, st>>>(mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, dq_acc);
+    main_bwd_dq_bf16_kernel<128><<<grid, 512, 0, st>>>(mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, dq_acc);
   else
-    main_bwd_dq_bf16_kernel<64><<<grid, 256, 0, st>>>(mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, dq_acc);
+    main_bwd_dq_bf16_kernel<64><<<grid, 512, 0, st>>>(mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, dq_acc);
   return hipGetLastError();
 }
 
