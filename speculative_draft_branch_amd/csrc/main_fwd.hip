@@ -18,11 +18,13 @@
 //
 // Eight waves in two groups of four, one group per query tile, two waves per
 // SIMD. Each group alternates a matrix phase (P V of the previous K/V tile, then
-// S of the current one) with a softmax phase, and the groups run one phase
-// apart, separated by workgroup barriers: while one group's exponentials occupy
-// the vector ALUs the other group's MFMAs keep the matrix cores busy. K and V
-// tiles are double-buffered and written straight into LDS by global_load_lds;
-// a tile is requested two phases before its first use.
+// S of the current one) with a softmax phase, and the groups start each tile
+// one phase apart (group 0 on its matrix phase, group 1 on its softmax phase):
+// while one group's exponentials occupy the vector ALUs the other group's MFMAs
+// keep the matrix cores busy. One workgroup barrier per tile; within the tile
+// each group moves on to its second phase as soon as its first is done. K and
+// V tiles are double-buffered and written straight into LDS by
+// global_load_lds; a tile is requested two phases before its first use.
 //
 // Per wave (32 query rows): S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so each
 // lane owns one query row (lane % 32) and row max/sum need a single exchange
@@ -312,8 +314,10 @@ __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf
           if (js >= 0 && js < ntiles && k_first + js * BN <= st.wmax)
             fwd_softmax<HD, RING>(st, s, k_first + js * BN, sl2, pb);
         }
-        if (h2 == 0) dma_barrier<63>();
-        else dma_barrier<0>();
+        // Only the end of the tile needs a barrier (the next requests reuse
+        // buffers read in this tile); a second one between the phases, which
+        // only kept the groups in step, cost 1.2%.
+        if (h2 == 1) dma_barrier<0>();
       }
     }
   }
