@@ -40,12 +40,16 @@ class ClockSampler:
     """Shader clock during the timed steps: a thread polls `amd-smi metric
     --clock --json` (the current gfx clock of every XCD) and keeps the mean of
     the clocks that are active (above 1 GHz). None when the tool is missing or
-    its output cannot be read."""
+    its output cannot be read, when disabled, and under a profiler: a
+    preloaded profiler library would initialise the GPU inside the tool's
+    process before that process execs its interpreter, and such an exec is
+    not allowed."""
 
-    def __init__(self):
+    def __init__(self, enabled=True):
         import shutil
         import threading
-        self.tool = shutil.which("amd-smi")
+        preload = os.environ.get("LD_PRELOAD", "") + os.environ.get("HSA_TOOLS_LIB", "")
+        self.tool = shutil.which("amd-smi") if enabled and "rocprof" not in preload else None
         self.samples = []
         self.stop = threading.Event()
         self.thread = threading.Thread(target=self._run, daemon=True)
@@ -258,6 +262,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ring-sim", action="store_true",
                     help="skip the ring-step simulation measured after the timed steps")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="do not sample the shader clock (amd-smi) during the timed steps")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before the warmup, copy a buffer of this many MiB once (a plain copy kernel of known "
                          "size, for scaling hardware byte counters); not part of the timed region")
@@ -319,7 +325,7 @@ def main():
     sda.timing_enable(True)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with ClockSampler() as clk:
+    with ClockSampler(enabled=not args.no_clock) as clk:
         e0.record(stream)
         for i in range(args.steps):
             step()
