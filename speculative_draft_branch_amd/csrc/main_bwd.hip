@@ -389,15 +389,23 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
         dp[b] = nd;
       }
       __builtin_amdgcn_s_setprio(1);  // a wave in an MFMA stretch wins issue; the other wave's VALU fills in
+      // The operands of step ks + 1 are read while step ks multiplies.
+      bf16x8 aq[2], ao[2];
+      aq[0] = pad_row_read<HD>(sQ, st.r_base, rb, 0);
+      ao[0] = pad_row_read<HD>(sdO, st.r_base, rb, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 aq = pad_row_read<HD>(sQ, st.r_base, rb, ks);
-        const bf16x8 ao = pad_row_read<HD>(sdO, st.r_base, rb, ks);
+        if (ks + 1 < KS) {
+          aq[(ks + 1) & 1] = pad_row_read<HD>(sQ, st.r_base, rb, ks + 1);
+          ao[(ks + 1) & 1] = pad_row_read<HD>(sdO, st.r_base, rb, ks + 1);
+        }
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
-          sc[b] = mfma32(aq, st.kf[b][ks], sc[b]);
-          dp[b] = mfma32(ao, st.vf[b][ks], dp[b]);
+          sc[b] = mfma32(aq[ks & 1], st.kf[b][ks], sc[b]);
+          dp[b] = mfma32(ao[ks & 1], st.vf[b][ks], dp[b]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_setprio(0);
 #pragma unroll
@@ -421,18 +429,33 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
     // dV += P^T dO, dK += dS^T Q over these 32 rows (two 16-row k-steps).
     // Operand slot 8*half + 4c + j <-> row 32rb + 16kh + 8c + 4*half + j.
     __builtin_amdgcn_s_setprio(1);
+    {
+      // Steps n = (kh, dt); the operands of step n + 1 are read while step n
+      // multiplies.
+      auto rdo = [&](int n) {
+        const int kk = 2 * rb + n / DT, dt = n % DT;
+        return join(pad_tr_read<HD>(sdO, st.t_base, 0, kk, dt), pad_tr_read<HD>(sdO, st.t_base, 1, kk, dt));
+      };
+      auto rdq = [&](int n) {
+        const int kk = 2 * rb + n / DT, dt = n % DT;
+        return join(pad_tr_read<HD>(sQ, st.t_base, 0, kk, dt), pad_tr_read<HD>(sQ, st.t_base, 1, kk, dt));
+      };
+      bf16x8 bo[2], bq[2];
+      bo[0] = rdo(0);
+      bq[0] = rdq(0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int kk = 2 * rb + kh;
-        const bf16x8 bo = join(pad_tr_read<HD>(sdO, st.t_base, 0, kk, dt), pad_tr_read<HD>(sdO, st.t_base, 1, kk, dt));
-        const bf16x8 bq = join(pad_tr_read<HD>(sQ, st.t_base, 0, kk, dt), pad_tr_read<HD>(sQ, st.t_base, 1, kk, dt));
+      for (int n = 0; n < 2 * DT; ++n) {
+        if (n + 1 < 2 * DT) {
+          bo[(n + 1) & 1] = rdo(n + 1);
+          bq[(n + 1) & 1] = rdq(n + 1);
+        }
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
-          st.adv[b][dt] = mfma32(pa[b][kh], bo, st.adv[b][dt]);
-          st.adk[b][dt] = mfma32(dsa[b][kh], bq, st.adk[b][dt]);
+          st.adv[b][n % DT] = mfma32(pa[b][n / DT], bo[n & 1], st.adv[b][n % DT]);
+          st.adk[b][n % DT] = mfma32(dsa[b][n / DT], bq[n & 1], st.adk[b][n % DT]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_s_setprio(0);
