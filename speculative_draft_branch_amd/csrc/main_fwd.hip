@@ -67,7 +67,7 @@ struct FwdState {
 // The phase is one software pipeline of (LDS read, MFMA) steps: the operands
 // of the next kRing steps are always in flight, so LDS latency is paid about
 // once per phase rather than once per k-step.
-constexpr int kRing = 4;
+constexpr int kRing = 6;
 
 template <int HD, bool PV, bool S>
 __device__ __forceinline__ void fwd_mphase(FwdState<HD> &st, const bf16 *sVt, const bf16 *sK, const bf16x8 (&pb)[4],
