@@ -92,6 +92,7 @@ Meta make_meta(const ba_plan *pl, const void *ws) {
   m.qtiles = reinterpret_cast<const QTile *>(b + L.qtiles);
   m.fwd_order = reinterpret_cast<const int32_t *>(b + L.fwd_order);
   m.fwd_pairs = reinterpret_cast<const int32_t *>(b + L.fwd_pairs);
+  m.fwd_triples = reinterpret_cast<const int32_t *>(b + L.fwd_triples);
   m.tile_row_id = reinterpret_cast<const int32_t *>(b + L.tile_row_id);
   m.tile_row_end = reinterpret_cast<const int32_t *>(b + L.tile_row_end);
   m.row_lo = reinterpret_cast<const int32_t *>(b + L.row_lo);
@@ -114,6 +115,7 @@ Meta make_meta(const ba_plan *pl, const void *ws) {
   m.n_qtiles = pl->n_qtiles;
   m.n_ktiles = pl->n_ktiles;
   m.n_fwd_pairs = pl->n_fwd_pairs;
+  m.n_fwd_triples = pl->n_fwd_triples;
   m.n_vt_tiles = pl->n_vt_tiles;
   m.max_branch = pl->max_branch;
   m.scale = pl->scale;

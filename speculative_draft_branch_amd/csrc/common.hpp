@@ -25,6 +25,7 @@ struct Meta {
   const QTile *qtiles;
   const int32_t *fwd_order;
   const int32_t *fwd_pairs;
+  const int32_t *fwd_triples;
   const int32_t *tile_row_id;
   const int32_t *tile_row_end;
   const int32_t *row_lo;
@@ -37,7 +38,7 @@ struct Meta {
   const int32_t *vt_base;
   int64_t N, Nq, Rb, A;
   int32_t hq, hkv, G, d, rows_per_tile;
-  int32_t n_qtiles, n_ktiles, n_fwd_pairs, n_vt_tiles;
+  int32_t n_qtiles, n_ktiles, n_fwd_pairs, n_vt_tiles, n_fwd_triples;
   int32_t max_branch;  // longest branch (rows of one anchor)
   float scale;
 };

@@ -185,8 +185,12 @@ __device__ __forceinline__ void load_k_tile(const Tile &kt, bf16 *dst, const bf1
 // [win_lo, win_hi) are attended; k holds exactly those rows (row 0 = position
 // win_lo) and vt their V^T tiles; every row's partial is merged into the
 // running float32 (o_run [Nq+Rb][Hq][d], lse_run [Hq][Nq+Rb]) in the epilogue.
-template <int HD, bool RING>
-__global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
+// NG: groups of four waves, one query tile each. With NG = 3 (the d = 64
+// forward, whose softmax phase is twice its matrix phase) two groups run their
+// softmax beside the third group's MFMAs, which gives the vector units of a
+// SIMD a third more throughput than one softmax wave gets there.
+template <int HD, bool RING, int NG>
+__global__ __launch_bounds__(256 * NG, 1) void main_fwd_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
                                                             const bf16 *__restrict__ qb,
                                                             const bf16 *__restrict__ k,
                                                             const bf16 *__restrict__ vt, bf16 *__restrict__ o,
@@ -201,13 +205,22 @@ __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf
   __shared__ __attribute__((aligned(16))) bf16 sV1[BN * HD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int grpi = wave >> 2;  // ping-pong group: 0 runs one phase ahead of 1
+  const int grpi = wave >> 2;  // group: 0 runs one phase ahead of the others
+  const int gp = grpi == 0 ? 0 : 1;  // the phase order of the wave's group
   const int hkv = mt.hkv, G = mt.G;
   const int g = blockIdx.x % hkv;
-  const int pair = blockIdx.x / hkv;
-  const int ta = uni(mt.fwd_pairs[2 * pair]), tb = uni(mt.fwd_pairs[2 * pair + 1]);
+  const int unit = blockIdx.x / hkv;
+  int tl[NG];
+#pragma unroll
+  for (int u = 0; u < NG; ++u) tl[u] = uni(NG == 2 ? mt.fwd_pairs[2 * unit + u] : mt.fwd_triples[NG * unit + u]);
+  const int ta = tl[0];
   const QTile tile_a = load_qtile(mt.qtiles + ta);
-  const int end_b = tb >= 0 ? uni(mt.qtiles[tb].end_max) : -1;
+  int end_b = -1;
+#pragma unroll
+  for (int u = 1; u < NG; ++u)
+    if (tl[u] >= 0) end_b = max(end_b, uni(mt.qtiles[tl[u]].end_max));
+  // With NG = 3 the DMA of a 64 x 64 tile (eight 1 KB blocks) is issued by waves 0-7.
+  const bool dma_wave = NG == 2 || wave < 8;
   // Keys [k_first + 64j, ...) for j < ntiles; k_first is the sequence start, or
   // in a ring step the start of the sequence's 64-key tile holding the window
   // start (tile t0 of the sequence), and keys before klo are masked.
@@ -228,7 +241,7 @@ __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf
   const int bi = mrow / G, hj = mrow - bi * G;
   int row = -1;
   st.end = -1;
-  const int my_tile = grpi ? tb : ta;
+  const int my_tile = grpi == 0 ? tl[0] : grpi == 1 ? tl[1] : tl[NG - 1];
   if (my_tile >= 0) {
     const QTile tile = load_qtile(mt.qtiles + my_tile);
     if (bi < tile.nrows) {
@@ -276,7 +289,7 @@ __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf
   // K rows are addressed relative to the buffer's first position (the window
   // start in a ring step); a ring step's first tile may begin before it.
   const int kb0 = RING ? win_lo : 0;
-  if (ntiles > 0) load_k_tile<RING>(kt, sK0, kg, k_first, kb0, klo, kv_end);
+  if (ntiles > 0 && dma_wave) load_k_tile<RING>(kt, sK0, kg, k_first, kb0, klo, kv_end);
   dma_barrier<0>();
 
   // Phase slots: slot t runs, for group grpi, local phase u = t - grpi; even u
@@ -296,12 +309,12 @@ __global__ __launch_bounds__(512, 1) void main_fwd_bf16_kernel(Meta mt, const bf
       bf16 *const sVc = par ? sV1 : sV0, *const sVp = par ? sV0 : sV1;
       // slot 2jj: requests, then group 0 matrix phase of jj, group 1 softmax of jj-1
       if (2 * jj >= nslots) goto done;
-      if (jj + 1 < ntiles) load_k_tile<RING>(kt, sKn, kg, k_first + (jj + 1) * BN, kb0, klo, kv_end);
-      if (jj < ntiles) vtt.load(sVc, vtg + jj * vt_stride, 0, HD - 1);
+      if (jj + 1 < ntiles && dma_wave) load_k_tile<RING>(kt, sKn, kg, k_first + (jj + 1) * BN, kb0, klo, kv_end);
+      if (jj < ntiles && dma_wave) vtt.load(sVc, vtg + jj * vt_stride, 0, HD - 1);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         if (h2 == 1 && 2 * jj + 1 >= nslots) goto done;
-        if (grpi == h2) {  // matrix phase of tile jj
+        if (gp == h2) {  // matrix phase of tile jj
           const bool do_pv = jj >= 1 && jj <= ntiles && k_first + (jj - 1) * BN <= st.wmax;
           const bool do_s = jj < ntiles && k_first + jj * BN <= st.wmax;
           __builtin_amdgcn_s_setprio(1);  // the matrix wave wins issue arbitration over the softmax wave
@@ -424,14 +437,14 @@ __global__ __launch_bounds__(256) void vt_transpose_bf16_kernel(Meta mt, const b
 // Every variant is instantiated explicitly: with two values of the bool
 // parameter launched from this file, this hipcc emitted the host launch stubs
 // of only one of them (the other launch then referenced an undefined stub).
-#define BA_FWD_INSTANCE(HD, RING)                                                                                \
-  template __global__ void main_fwd_bf16_kernel<HD, RING>(Meta, const bf16 *, const bf16 *, const bf16 *,        \
-                                                          const bf16 *, bf16 *, float *, float *, float *, int, int, \
-                                                          float *, float *)
-BA_FWD_INSTANCE(128, false);
-BA_FWD_INSTANCE(64, false);
-BA_FWD_INSTANCE(128, true);
-BA_FWD_INSTANCE(64, true);
+#define BA_FWD_INSTANCE(HD, RING, NG)                                                                            \
+  template __global__ void main_fwd_bf16_kernel<HD, RING, NG>(Meta, const bf16 *, const bf16 *, const bf16 *,    \
+                                                              const bf16 *, bf16 *, float *, float *, float *, int, \
+                                                              int, float *, float *)
+BA_FWD_INSTANCE(128, false, 2);
+BA_FWD_INSTANCE(64, false, 3);
+BA_FWD_INSTANCE(128, true, 2);
+BA_FWD_INSTANCE(64, true, 2);
 #undef BA_FWD_INSTANCE
 
 hipError_t launch_vt_transpose_bf16(const Meta &mt, const bf16 *v, bf16 *vt, hipStream_t st, int win_lo,
@@ -448,13 +461,12 @@ hipError_t launch_vt_transpose_bf16(const Meta &mt, const bf16 *v, bf16 *vt, hip
 hipError_t launch_main_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *vt,
                                 bf16 *o, float *lse, float *o_pre, float *lse_pre, hipStream_t st) {
   if (mt.n_fwd_pairs == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv);
   if (mt.d == 128)
-    main_fwd_bf16_kernel<128, false><<<grid, 512, 0, st>>>(mt, q, qb, k, vt, o, lse, o_pre, lse_pre, 0, 0, nullptr,
-                                                           nullptr);
+    main_fwd_bf16_kernel<128, false, 2><<<(unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv), 512, 0, st>>>(
+        mt, q, qb, k, vt, o, lse, o_pre, lse_pre, 0, 0, nullptr, nullptr);
   else
-    main_fwd_bf16_kernel<64, false><<<grid, 512, 0, st>>>(mt, q, qb, k, vt, o, lse, o_pre, lse_pre, 0, 0, nullptr,
-                                                          nullptr);
+    main_fwd_bf16_kernel<64, false, 3><<<(unsigned)((int64_t)mt.n_fwd_triples * mt.hkv), 768, 0, st>>>(
+        mt, q, qb, k, vt, o, lse, o_pre, lse_pre, 0, 0, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -463,10 +475,10 @@ hipError_t launch_ring_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, c
   if (mt.n_fwd_pairs == 0 || win_lo >= win_hi) return hipSuccess;
   const unsigned grid = (unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv);
   if (mt.d == 128)
-    main_fwd_bf16_kernel<128, true><<<grid, 512, 0, st>>>(mt, q, qb, k_win, vt, nullptr, nullptr, nullptr, nullptr,
+    main_fwd_bf16_kernel<128, true, 2><<<grid, 512, 0, st>>>(mt, q, qb, k_win, vt, nullptr, nullptr, nullptr, nullptr,
                                                           win_lo, win_hi, o_run, lse_run);
   else
-    main_fwd_bf16_kernel<64, true><<<grid, 512, 0, st>>>(mt, q, qb, k_win, vt, nullptr, nullptr, nullptr, nullptr,
+    main_fwd_bf16_kernel<64, true, 2><<<grid, 512, 0, st>>>(mt, q, qb, k_win, vt, nullptr, nullptr, nullptr, nullptr,
                                                          win_lo, win_hi, o_run, lse_run);
   return hipGetLastError();
 }

@@ -212,32 +212,36 @@ void build(ba_plan *pl) {
     return ca > cb;
   });
 
-  // Forward workgroups take two consecutive tiles of one sequence (their prefix
-  // ends are adjacent in the sorted order, so they share almost every K/V tile);
-  // cost is the longer key range of the two.
-  std::vector<int32_t> fwd_pairs;
-  std::vector<int64_t> pair_cost;
-  for (int32_t s = 0; s < pl->S; ++s) {
-    for (int32_t a = seq_qt_begin[s]; a < seq_qt_begin[s + 1]; a += 2) {
-      const int32_t b = a + 1 < seq_qt_begin[s + 1] ? a + 1 : -1;
-      fwd_pairs.push_back(a);
-      fwd_pairs.push_back(b);
-      const int32_t e = b >= 0 ? std::max(qt[a].end_max, qt[b].end_max) : qt[a].end_max;
-      pair_cost.push_back((int64_t)e - qt[a].kv_lo + 1);
+  // Forward workgroups take U consecutive tiles of one sequence (their prefix
+  // ends are adjacent in the sorted order, so they share almost every K/V tile;
+  // -1 where the sequence runs out); cost is the longest key range among them.
+  // Units are listed longest first. Pairs serve the d = 128 forward and the dQ
+  // kernel, threes the d = 64 forward.
+  auto fwd_units = [&](int32_t U, int32_t &n_units) {
+    std::vector<int32_t> units;
+    std::vector<int64_t> cost;
+    for (int32_t s = 0; s < pl->S; ++s) {
+      for (int32_t a = seq_qt_begin[s]; a < seq_qt_begin[s + 1]; a += U) {
+        int32_t e = qt[a].end_max;
+        for (int32_t u = 0; u < U; ++u) {
+          const int32_t t = a + u < seq_qt_begin[s + 1] ? a + u : -1;
+          units.push_back(t);
+          if (t >= 0) e = std::max(e, qt[t].end_max);
+        }
+        cost.push_back((int64_t)e - qt[a].kv_lo + 1);
+      }
     }
-  }
-  pl->n_fwd_pairs = (int32_t)pair_cost.size();
-  {
-    std::vector<int32_t> ord(pair_cost.size());
+    n_units = (int32_t)cost.size();
+    std::vector<int32_t> ord(cost.size());
     std::iota(ord.begin(), ord.end(), 0);
-    std::stable_sort(ord.begin(), ord.end(), [&](int32_t x, int32_t y) { return pair_cost[x] > pair_cost[y]; });
-    std::vector<int32_t> sorted(fwd_pairs.size());
-    for (size_t i = 0; i < ord.size(); ++i) {
-      sorted[2 * i] = fwd_pairs[2 * (size_t)ord[i]];
-      sorted[2 * i + 1] = fwd_pairs[2 * (size_t)ord[i] + 1];
-    }
-    fwd_pairs.swap(sorted);
-  }
+    std::stable_sort(ord.begin(), ord.end(), [&](int32_t x, int32_t y) { return cost[x] > cost[y]; });
+    std::vector<int32_t> sorted(units.size());
+    for (size_t i = 0; i < ord.size(); ++i)
+      for (int32_t u = 0; u < U; ++u) sorted[U * i + u] = units[U * (size_t)ord[i] + u];
+    return sorted;
+  };
+  std::vector<int32_t> fwd_pairs = fwd_units(2, pl->n_fwd_pairs);
+  std::vector<int32_t> fwd_triples = fwd_units(3, pl->n_fwd_triples);
 
   // Backward key tiles: per sequence, kBwdKeys main keys each; the query tiles
   // that see a key tile are the sequence's tiles whose largest end reaches it.
@@ -290,6 +294,7 @@ void build(ba_plan *pl) {
   L.qtiles = put(blob, cur, qt);
   L.fwd_order = put(blob, cur, fwd_order);
   L.fwd_pairs = put(blob, cur, fwd_pairs);
+  L.fwd_triples = put(blob, cur, fwd_triples);
   L.tile_row_id = put(blob, cur, trow_id);
   L.tile_row_end = put(blob, cur, trow_end);
   L.row_lo = put(blob, cur, row_lo);

@@ -49,6 +49,7 @@ struct BlobLayout {
   size_t qtiles;        // QTile [n_qtiles], sequence order
   size_t fwd_order;     // int32 [n_qtiles]: longest-first launch order
   size_t fwd_pairs;     // int32 [n_fwd_pairs][2]: tiles sharing a forward workgroup (-1 = none), longest first
+  size_t fwd_triples;   // int32 [n_fwd_triples][3]: the same in threes (the d = 64 forward), longest first
   size_t tile_row_id;   // int32 [n_qtiles * rows_per_tile]: combined row id, -1 = padding
   size_t tile_row_end;  // int32 [n_qtiles * rows_per_tile]: prefix end of that row
   size_t row_lo;        // int32 [Nq + Rb]: first visible main key of each combined row
@@ -75,7 +76,7 @@ struct ba_plan {
   std::vector<uint8_t> mode;
   int32_t rows_per_tile;  // base rows per query tile
   int32_t max_branch;     // longest branch (rows of one anchor)
-  int32_t n_qtiles, n_ktiles, n_fwd_pairs, n_vt_tiles;
+  int32_t n_qtiles, n_ktiles, n_fwd_pairs, n_vt_tiles, n_fwd_triples;
   int64_t pairs[3];
   ba::BlobLayout layout;
   std::vector<uint8_t> blob;  // host copy of the device metadata
