@@ -117,8 +117,11 @@ __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const b
 
 }  // namespace
 
-template <int HD>
-__global__ __launch_bounds__(512, 1) void main_bwd_dq_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
+// NG: groups of four waves, one query tile each (the forward's work unit): two
+// at d = 128, three at d = 64, where three waves per SIMD fit in the registers
+// and the vector work of one wave's tile meets the MFMAs of two others.
+template <int HD, int NG>
+__global__ __launch_bounds__(256 * NG, 1) void main_bwd_dq_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
                                                                const bf16 *__restrict__ qb,
                                                                const bf16 *__restrict__ k,
                                                                const bf16 *__restrict__ v,
@@ -143,25 +146,35 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_bf16_kernel(Meta mt, const
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hkv = mt.hkv, G = mt.G;
   const int g = blockIdx.x % hkv;
-  const int pair = blockIdx.x / hkv;
-  const int ta = uni(mt.fwd_pairs[2 * pair]), tb = uni(mt.fwd_pairs[2 * pair + 1]);
-  const QTile tile_a = load_qtile(mt.qtiles + ta);
-  const int end_b = tb >= 0 ? uni(mt.qtiles[tb].end_max) : -1;
+  const int unit = blockIdx.x / hkv;
+  int tl[NG];
+#pragma unroll
+  for (int u = 0; u < NG; ++u) tl[u] = uni(NG == 2 ? mt.fwd_pairs[2 * unit + u] : mt.fwd_triples[NG * unit + u]);
+  const QTile tile_a = load_qtile(mt.qtiles + tl[0]);
+  int end_b = -1;
+#pragma unroll
+  for (int u = 1; u < NG; ++u)
+    if (tl[u] >= 0) end_b = max(end_b, uni(mt.qtiles[tl[u]].end_max));
+  // With NG = 3 the DMA of a 64 x 64 tile (eight 1 KB blocks) is issued by waves 0-7.
+  const bool dma_wave = NG == 2 || wave < 8;
   const int64_t R = mt.Nq + mt.Rb;
   const int kv_lo = tile_a.kv_lo, kv_end = max(tile_a.end_max, end_b);
   const int ntiles = (kv_end - kv_lo + BN) / BN;
   AsyncTile<HD, BN, 512> kvt;
   kvt.init(hkv * HD, tid);
   const bf16 *kg = k + (int64_t)g * HD, *vg = v + (int64_t)g * HD;
-  kvt.load(sK0, kg, kv_lo, kv_end);
-  kvt.load(sV0, vg, kv_lo, kv_end);
+  if (dma_wave) {
+    kvt.load(sK0, kg, kv_lo, kv_end);
+    kvt.load(sV0, vg, kv_lo, kv_end);
+  }
 
   DqState<HD> st;
   const int mrow = (wave & 3) * 32 + (lane & 31);
   const int bi = mrow / G, hj = mrow - bi * G;
   int row = -1;
   st.end = -1;
-  const int my_tile = (wave >> 2) ? tb : ta;
+  const int grpi = wave >> 2;
+  const int my_tile = grpi == 0 ? tl[0] : grpi == 1 ? tl[1] : tl[NG - 1];
   if (my_tile >= 0) {
     const QTile tile = load_qtile(mt.qtiles + my_tile);
     if (bi < tile.nrows) {
@@ -209,7 +222,7 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_bf16_kernel(Meta mt, const
   for (int j = 0; j < ntiles; j += 2) {
     const int k0 = kv_lo + j * BN;
     dma_barrier<0>();  // tile j is in buffer 0; every wave is done with buffer 1
-    if (j + 1 < ntiles) {
+    if (j + 1 < ntiles && dma_wave) {
       kvt.load(sK1, kg, k0 + BN, kv_end);
       kvt.load(sV1, vg, k0 + BN, kv_end);
     }
@@ -219,7 +232,7 @@ __global__ __launch_bounds__(512, 1) void main_bwd_dq_bf16_kernel(Meta mt, const
     }
     if (j + 1 >= ntiles) break;
     dma_barrier<0>();  // tile j+1 is in buffer 1; every wave is done with buffer 0
-    if (j + 2 < ntiles) {
+    if (j + 2 < ntiles && dma_wave) {
       kvt.load(sK0, kg, k0 + 2 * BN, kv_end);
       kvt.load(sV0, vg, k0 + 2 * BN, kv_end);
     }
@@ -596,11 +609,12 @@ hipError_t launch_main_bwd_dq_bf16(const Meta &mt, const bf16 *q, const bf16 *qb
                                    const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
                                    const float *delta, float *dq_acc, hipStream_t st) {
   if (mt.n_fwd_pairs == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv);
   if (mt.d == 128)
-    main_bwd_dq_bf16_kernel<128><<<grid, 512, 0, st>>>(mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, dq_acc);
+    main_bwd_dq_bf16_kernel<128, 2><<<(unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv), 512, 0, st>>>(
+        mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, dq_acc);
   else
-    main_bwd_dq_bf16_kernel<64><<<grid, 512, 0, st>>>(mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, dq_acc);
+    main_bwd_dq_bf16_kernel<64, 3><<<(unsigned)((int64_t)mt.n_fwd_triples * mt.hkv), 768, 0, st>>>(
+        mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, dq_acc);
   return hipGetLastError();
 }
 
