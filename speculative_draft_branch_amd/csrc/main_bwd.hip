@@ -345,11 +345,13 @@ __global__ __launch_bounds__(256) void bwd_gather_bf16_kernel(Meta mt, const bf1
 
 namespace {
 
-// Keys per wave: KB blocks of 32; eight waves of one block each give two waves
-// per SIMD within the 256-register budget (K, V fragments and the dK, dV
-// accumulators alone hold 192 registers at d = 128).
+// Keys per wave: KB blocks of 32. At d = 128 eight waves of one block each
+// give two waves per SIMD within the 256-register budget (K, V fragments and
+// the dK, dV accumulators alone hold 192 registers); at d = 64 a wave needs
+// about 164, so twelve waves (three per SIMD, 384 keys) fit, and each wave's
+// elementwise work has two other waves' MFMAs beside it.
 constexpr int kDkdvBlocks = 1;
-constexpr int kDkdvThreads = 64 * kBwdKeys / (32 * kDkdvBlocks);
+constexpr int dkdv_threads(int hd) { return 64 * (hd == 64 ? kBwdKeys64 : kBwdKeys) / (32 * kDkdvBlocks); }
 
 template <int HD, int KB>
 struct DkdvState {
@@ -492,7 +494,7 @@ __device__ __forceinline__ void dkdv_tile(DkdvState<HD, KB> &st, const bf16 *sQ,
 }  // namespace
 
 template <int HD>
-__global__ __launch_bounds__(kDkdvThreads, 1) void main_bwd_dkdv_bf16_kernel(Meta mt, const bf16 *__restrict__ k,
+__global__ __launch_bounds__(dkdv_threads(HD), 1) void main_bwd_dkdv_bf16_kernel(Meta mt, const bf16 *__restrict__ k,
                                                                           const bf16 *__restrict__ v,
                                                                           const bf16 *__restrict__ qt_rows,
                                                                           const bf16 *__restrict__ do_rows,
@@ -501,9 +503,10 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void main_bwd_dkdv_bf16_kernel(Met
                                                                           const int *__restrict__ et,
                                                                           bf16 *__restrict__ dk, bf16 *__restrict__ dv) {
   constexpr int BM = kTileRows;  // 128 MFMA rows per query tile
-  constexpr int KB = kDkdvBlocks, NT = kDkdvThreads;
+  constexpr int KB = kDkdvBlocks, NT = dkdv_threads(HD);
   constexpr int KS = HD / 16, DT = HD / 32;
-  static_assert(kBwdKeys == 32 * KB * (NT / 64) && BM == 128, "tile shape");
+  static_assert((HD == 64 ? kBwdKeys64 : kBwdKeys) == 32 * KB * (NT / 64) && BM == 128, "tile shape");
+  constexpr int NSW = 8;  // waves that stage the Q and dO rows (128 rows split evenly)
   // Padded tiles (see stage_padded_async). Q and dO of one buffer share an
   // array, so a read of either is one address plus a constant offset.
   constexpr int TILE = BM * kPadRowBytes<HD> / 2;  // elements per padded tile
@@ -528,8 +531,10 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void main_bwd_dkdv_bf16_kernel(Met
     if (wave == 0) stage_words_async<BM / 64>(sL, lt + tb, lane);
     else if (wave == 1) stage_words_async<BM / 64>(sD, dtt + tb, lane);
     else if (wave == 2) stage_words_async<kTileMetaWords / 64>(sE, et + (int64_t)qi * kTileMetaWords, lane);
-    stage_padded_async<HD, BM, NT / 64>(sQ, qt_rows + tb * HD, wave, lane);
-    stage_padded_async<HD, BM, NT / 64>(sO, do_rows + tb * HD, wave, lane);
+    if (NT / 64 == NSW || wave < NSW) {
+      stage_padded_async<HD, BM, NSW>(sQ, qt_rows + tb * HD, wave, lane);
+      stage_padded_async<HD, BM, NSW>(sO, do_rows + tb * HD, wave, lane);
+    }
   };
   if (kt.qt_begin < kt.qt_end) prefetch(kt.qt_begin, sQ0, sO0, sL0, sD0, sE0);
 
@@ -624,9 +629,9 @@ hipError_t launch_main_bwd_dkdv_bf16(const Meta &mt, const bf16 *k, const bf16 *
   if (mt.n_ktiles == 0) return hipSuccess;
   const unsigned grid = (unsigned)((int64_t)mt.n_ktiles * mt.hkv);
   if (mt.d == 128)
-    main_bwd_dkdv_bf16_kernel<128><<<grid, kDkdvThreads, 0, st>>>(mt, k, v, qt, dot, lt, dtt, et, dk, dv);
+    main_bwd_dkdv_bf16_kernel<128><<<grid, dkdv_threads(128), 0, st>>>(mt, k, v, qt, dot, lt, dtt, et, dk, dv);
   else
-    main_bwd_dkdv_bf16_kernel<64><<<grid, kDkdvThreads, 0, st>>>(mt, k, v, qt, dot, lt, dtt, et, dk, dv);
+    main_bwd_dkdv_bf16_kernel<64><<<grid, dkdv_threads(64), 0, st>>>(mt, k, v, qt, dot, lt, dtt, et, dk, dv);
   return hipGetLastError();
 }
 

@@ -243,18 +243,20 @@ void build(ba_plan *pl) {
   std::vector<int32_t> fwd_pairs = fwd_units(2, pl->n_fwd_pairs);
   std::vector<int32_t> fwd_triples = fwd_units(3, pl->n_fwd_triples);
 
-  // Backward key tiles: per sequence, kBwdKeys main keys each; the query tiles
-  // that see a key tile are the sequence's tiles whose largest end reaches it.
+  // Backward key tiles: per sequence, bwd_keys() main keys each; the query
+  // tiles that see a key tile are the sequence's tiles whose largest end
+  // reaches it.
+  const int32_t bk = bwd_keys(pl->dtype, pl->d);
   std::vector<KTile> kt;
   std::vector<int64_t> kt_cost;
   std::vector<int64_t> rows_prefix(qt.size() + 1, 0);
   for (size_t i = 0; i < qt.size(); ++i) rows_prefix[i + 1] = rows_prefix[i] + qt[i].nrows;
   for (int32_t s = 0; s < pl->S; ++s) {
     int32_t b0 = seq_qt_begin[s], b1 = seq_qt_begin[s + 1];
-    for (int32_t k0 = pl->cu[s]; k0 < pl->cu[s + 1]; k0 += kBwdKeys) {
+    for (int32_t k0 = pl->cu[s]; k0 < pl->cu[s + 1]; k0 += bk) {
       KTile t{};
       t.key_lo = k0;
-      t.key_hi = std::min(k0 + kBwdKeys, pl->cu[s + 1]);
+      t.key_hi = std::min(k0 + bk, pl->cu[s + 1]);
       int32_t lo = b0, hi = b1;  // first tile with end_max >= k0
       while (lo < hi) {
         int32_t mid = (lo + hi) / 2;

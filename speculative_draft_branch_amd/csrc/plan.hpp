@@ -13,8 +13,11 @@ namespace ba {
 
 // Rows per query tile in MFMA rows (base rows x q heads of one kv group).
 constexpr int kTileRows = 128;
-// Keys per backward key tile.
+// Keys per backward key tile: 256, except for the bf16 d = 64 dK/dV kernel,
+// whose twelve waves of 32 keys (three per SIMD) take 384.
 constexpr int kBwdKeys = 256;
+constexpr int kBwdKeys64 = 384;
+inline int bwd_keys(int dtype, int d) { return dtype == BA_BF16 && d == 64 ? kBwdKeys64 : kBwdKeys; }
 // Per-query-tile block of row ends the backward gather writes: 128 prefix ends,
 // then the tile's smallest end, largest end and valid MFMA rows (padded to 3 x 64
 // words for whole-wave LDS copies).
