@@ -364,9 +364,21 @@ ba_status_t branch_attn_bwd(const ba_plan_t *pl, const void *q, const void *k, c
       return launch_main_bwd_dq_bf16(mt, (const bf16 *)q, (const bf16 *)qb, (const bf16 *)k, (const bf16 *)v,
                                      (const bf16 *)d_o, (const bf16 *)d_ob, lse, lseb, delta, dq_acc, st);
     }));
+    // Split key tiles: every dK/dV workgroup adds into zeroed float32
+    // accumulators, converted to bf16 afterwards (a fill kernel, not a memset).
+    float *dkv_acc = pl->dkv_split ? reinterpret_cast<float *>(ws + pl->off_dkv_acc) : nullptr;
+    const int64_t nkv = pl->N * kd;
     BA_TRY(timed(K_MAIN_BWD_DKDV, st, "main-sequence backward (dk, dv)", [&] {
-      return launch_main_bwd_dkdv_bf16(mt, (const bf16 *)k, (const bf16 *)v, qt, dot, lt, dtt, et, (bf16 *)dk,
-                                       (bf16 *)dv, st);
+      if (dkv_acc) {
+        hipError_t e = launch_fill_f32(dkv_acc, 2 * nkv, 0.0f, st);
+        if (e != hipSuccess) return e;
+      }
+      hipError_t e = launch_main_bwd_dkdv_bf16(mt, (const bf16 *)k, (const bf16 *)v, qt, dot, lt, dtt, et,
+                                               (bf16 *)dk, (bf16 *)dv, dkv_acc, st);
+      if (e != hipSuccess || !dkv_acc) return e;
+      e = launch_convert_rows(dkv_acc, nkv, dk, pl->dtype, st);
+      if (e != hipSuccess) return e;
+      return launch_convert_rows(dkv_acc + nkv, nkv, dv, pl->dtype, st);
     }));
   } else {
     BA_TRY(timed(K_BWD_PREPROCESS, st, "backward preprocess",

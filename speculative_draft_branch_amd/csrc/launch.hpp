@@ -54,8 +54,10 @@ hipError_t launch_main_bwd_dq_bf16(const Meta &mt, const bf16 *q, const bf16 *qb
 hipError_t launch_bwd_gather_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *o, const bf16 *ob,
                                   const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
                                   float *delta, bf16 *qt, bf16 *dot, float *lt, float *dtt, int *et, hipStream_t st);
+// dkv_acc: null, or float32 dK, dV accumulators [N][Hkv][d] (zeroed) into
+// which every workgroup adds instead of writing dk, dv (plans with split key tiles).
 hipError_t launch_main_bwd_dkdv_bf16(const Meta &mt, const bf16 *k, const bf16 *v, const bf16 *qt, const bf16 *dot,
                                      const float *lt, const float *dtt, const int *et, bf16 *dk, bf16 *dv,
-                                     hipStream_t st);
+                                     float *dkv_acc, hipStream_t st);
 
 }  // namespace ba

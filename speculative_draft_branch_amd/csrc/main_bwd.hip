@@ -501,7 +501,8 @@ __global__ __launch_bounds__(dkdv_threads(HD), 1) void main_bwd_dkdv_bf16_kernel
                                                                           const float *__restrict__ lt,
                                                                           const float *__restrict__ dtt,
                                                                           const int *__restrict__ et,
-                                                                          bf16 *__restrict__ dk, bf16 *__restrict__ dv) {
+                                                                          bf16 *__restrict__ dk, bf16 *__restrict__ dv,
+                                                                          float *__restrict__ dkv_acc) {
   constexpr int BM = kTileRows;  // 128 MFMA rows per query tile
   constexpr int KB = kDkdvBlocks, NT = dkdv_threads(HD);
   constexpr int KS = HD / 16, DT = HD / 32;
@@ -580,6 +581,9 @@ __global__ __launch_bounds__(dkdv_threads(HD), 1) void main_bwd_dkdv_bf16_kernel
   // dK, dV of the wave's keys: element i of block (b, dt) is key wkey_lo +
   // 32b + (i/4)*8 + 4*(lane/32) + i%4, d = 32dt + lane%32. The staged Q rows
   // carry scale * log2(e), so dK = scale * dS^T Q = ln(2) * dS^T Q_staged.
+  // With split key tiles the float32 results are added into the accumulators
+  // (dK at dkv_acc, dV N * Hkv * d further on) instead.
+  const int64_t acc_v = (int64_t)mt.N * hkv * HD;
 #pragma unroll
   for (int b = 0; b < KB; ++b)
 #pragma unroll
@@ -589,8 +593,13 @@ __global__ __launch_bounds__(dkdv_threads(HD), 1) void main_bwd_dkdv_bf16_kernel
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const int64_t dst = ((int64_t)key * hkv + g) * HD + dt * 32 + (lane & 31);
-          dk[dst] = (bf16)(kLn2 * st.adk[b][dt][i]);
-          dv[dst] = (bf16)st.adv[b][dt][i];
+          if (dkv_acc) {
+            atomicAdd(dkv_acc + dst, kLn2 * st.adk[b][dt][i]);
+            atomicAdd(dkv_acc + acc_v + dst, st.adv[b][dt][i]);
+          } else {
+            dk[dst] = (bf16)(kLn2 * st.adk[b][dt][i]);
+            dv[dst] = (bf16)st.adv[b][dt][i];
+          }
         }
       }
     }
@@ -625,13 +634,15 @@ hipError_t launch_main_bwd_dq_bf16(const Meta &mt, const bf16 *q, const bf16 *qb
 
 hipError_t launch_main_bwd_dkdv_bf16(const Meta &mt, const bf16 *k, const bf16 *v, const bf16 *qt, const bf16 *dot,
                                      const float *lt, const float *dtt, const int *et, bf16 *dk, bf16 *dv,
-                                     hipStream_t st) {
+                                     float *dkv_acc, hipStream_t st) {
   if (mt.n_ktiles == 0) return hipSuccess;
   const unsigned grid = (unsigned)((int64_t)mt.n_ktiles * mt.hkv);
   if (mt.d == 128)
-    main_bwd_dkdv_bf16_kernel<128><<<grid, dkdv_threads(128), 0, st>>>(mt, k, v, qt, dot, lt, dtt, et, dk, dv);
+    main_bwd_dkdv_bf16_kernel<128><<<grid, dkdv_threads(128), 0, st>>>(mt, k, v, qt, dot, lt, dtt, et, dk, dv,
+                                                                        dkv_acc);
   else
-    main_bwd_dkdv_bf16_kernel<64><<<grid, dkdv_threads(64), 0, st>>>(mt, k, v, qt, dot, lt, dtt, et, dk, dv);
+    main_bwd_dkdv_bf16_kernel<64><<<grid, dkdv_threads(64), 0, st>>>(mt, k, v, qt, dot, lt, dtt, et, dk, dv,
+                                                                      dkv_acc);
   return hipGetLastError();
 }
 

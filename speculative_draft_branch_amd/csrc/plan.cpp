@@ -268,6 +268,41 @@ void build(ba_plan *pl) {
       kt_cost.push_back(rows_prefix[b1] - rows_prefix[lo]);
     }
   }
+  // A key tile whose query range costs more than a compute unit's share of the
+  // whole (Hkv workgroups per tile over 256 compute units) would set the
+  // kernel's end by itself: its range is split in two halves of equal rows,
+  // and then every dK/dV workgroup adds its float32 result into a zeroed
+  // accumulator (one add for a whole tile, two for a split one, exact in either
+  // order, so the result stays deterministic) that one pass converts to bf16.
+  pl->dkv_split = false;
+  if (pl->dtype == BA_BF16 && !kt.empty()) {
+    int64_t total = 0;
+    for (int64_t c : kt_cost) total += c;
+    const double share = (double)total * pl->hkv / 256.0;
+    std::vector<KTile> kt2;
+    std::vector<int64_t> cost2;
+    for (size_t i = 0; i < kt.size(); ++i) {
+      const KTile t = kt[i];
+      if ((double)kt_cost[i] > share && t.qt_end - t.qt_begin >= 2) {
+        const int64_t half = (rows_prefix[t.qt_begin] + rows_prefix[t.qt_end]) / 2;
+        int32_t mid = t.qt_begin + 1;
+        while (mid < t.qt_end - 1 && rows_prefix[mid] < half) ++mid;
+        KTile a = t, b = t;
+        a.qt_end = mid;
+        b.qt_begin = mid;
+        kt2.push_back(a);
+        cost2.push_back(rows_prefix[mid] - rows_prefix[t.qt_begin]);
+        kt2.push_back(b);
+        cost2.push_back(rows_prefix[t.qt_end] - rows_prefix[mid]);
+        pl->dkv_split = true;
+      } else {
+        kt2.push_back(t);
+        cost2.push_back(kt_cost[i]);
+      }
+    }
+    kt.swap(kt2);
+    kt_cost.swap(cost2);
+  }
   pl->n_ktiles = (int32_t)kt.size();
   std::vector<int32_t> bwd_order(kt.size());
   std::iota(bwd_order.begin(), bwd_order.end(), 0);
@@ -342,6 +377,11 @@ void build(ba_plan *pl) {
     cur_b = pl->off_et + align_up((size_t)pl->n_qtiles * kTileMetaWords * 4, 256);
   } else {
     pl->off_qt = pl->off_dot = pl->off_lt = pl->off_dt = pl->off_et = cur_b;
+  }
+  pl->off_dkv_acc = 0;
+  if (pl->dkv_split) {
+    pl->off_dkv_acc = cur_b;
+    cur_b += 2 * align_up((size_t)pl->N * pl->hkv * pl->d * f32, 256);
   }
   pl->ws_bwd = cur_b;
 }

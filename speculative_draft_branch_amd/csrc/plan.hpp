@@ -91,6 +91,10 @@ struct ba_plan {
   // backward, query-tile order per kv head: Q and dO rows [n_qtiles][Hkv][128][d],
   // LSE*log2(e) and D [n_qtiles][Hkv][128], row-end blocks [n_qtiles][kTileMetaWords]
   size_t off_qt, off_dot, off_lt, off_dt, off_et;
+  // backward, bf16, when some key tile's query range is split in two: float32
+  // dK and dV accumulators [N][Hkv][d] each (0 when nothing is split)
+  size_t off_dkv_acc;
+  bool dkv_split;
 };
 
 namespace ba {
