@@ -114,6 +114,34 @@ def test_workspace_sizes_cover_partials():
     assert 0 < p.workspace_bytes(2) <= p.workspace_bytes(0)
 
 
+def _key_tiles_unsplit(w):
+    bk = 384 if (w.dtype == "bf16" and w.head_dim == 64) else 256
+    cu = w.cu_seqlens
+    return sum(-(-int(cu[i + 1] - cu[i]) // bk) for i in range(len(cu) - 1))
+
+
+@pytest.mark.parametrize("name,splits", [("ctx256k_rank3", False), ("gptoss_128k_mixed", False),
+                                         ("qwen3_8b_16k", True), ("qwen3_8b_16k_div16", True)])
+def test_backward_key_tiles_split_only_where_one_tile_outweighs_a_units_share(name, splits):
+    """A bf16 plan splits a key tile's query range in two (never more) only when
+    that tile costs more than 1/256 of the whole kernel per kv head; such plans
+    carry float32 dK, dV accumulators in the backward workspace."""
+    w = W.get(name)
+    p = Plan.from_workload(w)
+    base = _key_tiles_unsplit(w)
+    n_split = p.n_ktiles - base
+    assert (n_split > 0) == splits and 0 <= n_split <= base
+    if splits:  # the backward workspace holds the two float32 accumulators
+        acc = 2 * w.N * w.num_kv_heads * w.head_dim * 4
+        assert p.workspace_bytes(1) > acc
+
+
+def test_float32_plans_never_split_key_tiles():
+    w = W.get("tiny_f32")
+    p = Plan.from_workload(w)
+    assert p.n_ktiles == _key_tiles_unsplit(w)
+
+
 def test_timing_api_without_launches():
     """The opt-in timing calls work on the host alone: names for every kernel id,
     zero totals when nothing was recorded, and argument checks."""
