@@ -277,64 +277,62 @@ __global__ __launch_bounds__(256) void bwd_gather_bf16_kernel(Meta mt, const bf1
                                                               float *__restrict__ delta, bf16 *__restrict__ qt,
                                                               bf16 *__restrict__ dot, float *__restrict__ lt,
                                                               float *__restrict__ dtt, int *__restrict__ et) {
-  constexpr int NCH = HD / 8;
+  // Coalesced: LPR lanes take the LPR 16-byte chunks of one row (a row of one
+  // head is contiguous), so each load instruction reads whole rows.
+  constexpr int LPR = HD / 8;          // lanes (16-byte chunks) per row
+  constexpr int RPP = 256 / LPR;       // rows per pass
   const int hkv = mt.hkv, G = mt.G;
   const int g = blockIdx.x % hkv;
   const int qi = blockIdx.x / hkv;
   const QTile tile = load_qtile(mt.qtiles + qi);
-  const int m = threadIdx.x >> 1, half = threadIdx.x & 1;
-  const int bi = m / G, hj = m - bi * G;
-  const int64_t trow = ((int64_t)qi * hkv + g) * kTileRows + m;
-  uint4 *qd = reinterpret_cast<uint4 *>(qt + trow * HD);
-  uint4 *od = reinterpret_cast<uint4 *>(dot + trow * HD);
-  const bool ok = bi < tile.nrows;
-  float dsum = 0.0f;
-  int row = 0, h = 0;
-  bool is_main = false;
-  if (ok) {
-    row = mt.tile_row_id[tile.row_begin + bi];
-    h = mt.group_heads[g * G + hj];
-    is_main = row < mt.Nq;
-    const int64_t off = is_main ? ((int64_t)row * mt.hq + h) * HD : ((int64_t)(row - mt.Nq) * mt.hq + h) * HD;
-    const uint4 *qs = reinterpret_cast<const uint4 *>((is_main ? q : qb) + off);
-    const uint4 *ds = reinterpret_cast<const uint4 *>((is_main ? d_o : d_ob) + off);
-    const uint4 *os = reinterpret_cast<const uint4 *>((is_main ? o : ob) + off);
-    const float sl2 = mt.scale * kLog2e;
-#pragma unroll
-    for (int c = 0; c < NCH / 2; ++c) {
-      const int ch = half * (NCH / 2) + c;
-      const bf16x8 xb = __builtin_bit_cast(bf16x8, qs[ch]);
+  const int ch = threadIdx.x % LPR, rsub = threadIdx.x / LPR;
+  const float sl2 = mt.scale * kLog2e;
+#pragma unroll 2
+  for (int pass = 0; pass < kTileRows / RPP; ++pass) {
+    const int m = pass * RPP + rsub;
+    const int bi = m / G, hj = m - bi * G;
+    const int64_t trow = ((int64_t)qi * hkv + g) * kTileRows + m;
+    uint4 *qd = reinterpret_cast<uint4 *>(qt + trow * HD);
+    uint4 *od = reinterpret_cast<uint4 *>(dot + trow * HD);
+    const bool ok = bi < tile.nrows;
+    float dsum = 0.0f;
+    int row = 0, h = 0;
+    bool is_main = false;
+    if (ok) {
+      row = mt.tile_row_id[tile.row_begin + bi];
+      h = mt.group_heads[g * G + hj];
+      is_main = row < mt.Nq;
+      const int64_t off = is_main ? ((int64_t)row * mt.hq + h) * HD : ((int64_t)(row - mt.Nq) * mt.hq + h) * HD;
+      const uint4 x = reinterpret_cast<const uint4 *>((is_main ? q : qb) + off)[ch];
+      const uint4 y = reinterpret_cast<const uint4 *>((is_main ? d_o : d_ob) + off)[ch];
+      const uint4 z = reinterpret_cast<const uint4 *>((is_main ? o : ob) + off)[ch];
+      const bf16x8 xb = __builtin_bit_cast(bf16x8, x);
       bf16x8 sq;
 #pragma unroll
       for (int e = 0; e < 8; ++e) sq[e] = (bf16)((float)xb[e] * sl2);
       qd[ch] = __builtin_bit_cast(uint4, sq);
-      const uint4 y = ds[ch];
       od[ch] = y;
-      const bf16x8 yb = __builtin_bit_cast(bf16x8, y);
-      const bf16x8 zb = __builtin_bit_cast(bf16x8, os[ch]);
+      const bf16x8 yb = __builtin_bit_cast(bf16x8, y), zb = __builtin_bit_cast(bf16x8, z);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dsum = fmaf((float)yb[e], (float)zb[e], dsum);
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < NCH / 2; ++c) {
-      const int ch = half * (NCH / 2) + c;
+    } else {
       qd[ch] = uint4{0u, 0u, 0u, 0u};
       od[ch] = uint4{0u, 0u, 0u, 0u};
     }
-  }
-  dsum += __shfl_xor(dsum, 1, 64);
-  if (half == 0) {
-    if (ok) {
-      const float l = is_main ? lse[(int64_t)h * mt.Nq + row] : lseb[(int64_t)h * mt.Rb + (row - mt.Nq)];
-      lt[trow] = -l * kLog2e;
-      dtt[trow] = -dsum;
-      delta[(int64_t)h * (mt.Nq + mt.Rb) + row] = dsum;
-    } else {
-      lt[trow] = -INFINITY;  // padding rows: P = 0
-      dtt[trow] = 0.0f;
+#pragma unroll
+    for (int sh = LPR / 2; sh >= 1; sh >>= 1) dsum += __shfl_xor(dsum, sh, 64);
+    if (ch == 0) {
+      if (ok) {
+        const float l = is_main ? lse[(int64_t)h * mt.Nq + row] : lseb[(int64_t)h * mt.Rb + (row - mt.Nq)];
+        lt[trow] = -l * kLog2e;
+        dtt[trow] = -dsum;
+        delta[(int64_t)h * (mt.Nq + mt.Rb) + row] = dsum;
+      } else {
+        lt[trow] = -INFINITY;  // padding rows: P = 0
+        dtt[trow] = 0.0f;
+      }
+      if (g == 0) et[(int64_t)qi * kTileMetaWords + m] = ok ? mt.tile_row_end[tile.row_begin + bi] : -1;
     }
-    if (g == 0) et[(int64_t)qi * kTileMetaWords + m] = ok ? mt.tile_row_end[tile.row_begin + bi] : -1;
   }
   if (g == 0 && threadIdx.x < kTileMetaWords - kTileRows) {
     const int w = threadIdx.x;
