@@ -36,55 +36,68 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-class ClockSampler:
-    """Shader clock during the timed steps: a thread polls `amd-smi metric
-    --clock --json` (the current gfx clock of every XCD) and keeps the mean of
-    the clocks that are active (above 1 GHz). None when the tool is missing or
-    its output cannot be read, when disabled, and under a profiler: a
-    preloaded profiler library would initialise the GPU inside the tool's
-    process before that process execs its interpreter, and such an exec is
-    not allowed."""
+def _sclk_path(pci=None):
+    """sysfs file that lists the shader clock levels of this process's GPU, with
+    the current one marked by '*': the PCI device of torch's device 0 when it
+    is known, else the only AMD card with such a file; None otherwise."""
+    import glob
+    if pci is not None:
+        p = "/sys/bus/pci/devices/%04x:%02x:%02x.0/pp_dpm_sclk" % pci
+        return p if os.path.exists(p) else None
+    found = []
+    for dev in glob.glob("/sys/class/drm/card*/device"):
+        try:
+            with open(os.path.join(dev, "vendor")) as f:
+                if f.read().strip() != "0x1002":
+                    continue
+        except OSError:
+            continue
+        if os.path.exists(os.path.join(dev, "pp_dpm_sclk")):
+            found.append(os.path.realpath(os.path.join(dev, "pp_dpm_sclk")))
+    found = sorted(set(found))
+    return found[0] if len(found) == 1 else None
 
-    def __init__(self, enabled=True):
-        import shutil
+
+def parse_sclk(text):
+    """Current shader clock in MHz from the text of pp_dpm_sclk (the line marked
+    '*', e.g. '1: 1900Mhz *'), or None."""
+    for line in text.splitlines():
+        if line.rstrip().endswith("*"):
+            tok = line.split(":", 1)[-1].strip().rstrip("*").strip().lower()
+            if tok.endswith("mhz"):
+                try:
+                    return float(tok[:-3])
+                except ValueError:
+                    return None
+    return None
+
+
+class ClockSampler:
+    """Shader clock during the timed steps, read in this process from sysfs
+    (pp_dpm_sclk of the GPU, polled every 0.2 s by a thread; no tool is
+    started): the mean of the samples above 1 GHz, or None when the file is
+    not there or not readable, or when disabled."""
+
+    def __init__(self, enabled=True, pci=None):
         import threading
-        preload = os.environ.get("LD_PRELOAD", "") + os.environ.get("HSA_TOOLS_LIB", "")
-        self.tool = shutil.which("amd-smi") if enabled and "rocprof" not in preload else None
+        self.path = _sclk_path(pci) if enabled else None
         self.samples = []
         self.stop = threading.Event()
         self.thread = threading.Thread(target=self._run, daemon=True)
 
-    def _read(self):
-        import subprocess
-        r = subprocess.run([self.tool, "metric", "--clock", "--json"], capture_output=True, text=True, timeout=20)
-        data = json.loads(r.stdout)
-        clks = []
-
-        def walk(x):
-            if isinstance(x, dict):
-                for k, v in x.items():
-                    if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict):
-                        val = v["clk"].get("value")
-                        if isinstance(val, (int, float)):
-                            clks.append(float(val))
-                    else:
-                        walk(v)
-            elif isinstance(x, list):
-                for v in x:
-                    walk(v)
-        walk(data)
-        return [c for c in clks if c > 1000.0]
-
     def _run(self):
         while not self.stop.is_set():
             try:
-                self.samples.extend(self._read())
-            except Exception:
+                with open(self.path) as f:
+                    v = parse_sclk(f.read())
+            except OSError:
                 return
+            if v is not None and v > 1000.0:
+                self.samples.append(v)
             self.stop.wait(0.2)
 
     def __enter__(self):
-        if self.tool:
+        if self.path:
             self.thread.start()
         return self
 
@@ -151,12 +164,101 @@ def row_pairs(w, rows):
     return out
 
 
-def cpu_baseline(w, t, seconds):
-    """The CPU oracle, as it is, on a bounded random sample of rows of the same
-    workload: forward of each sampled row plus its backward contributions."""
+def stratified_rows(w, n=512, seed=0):
+    """A seeded sample of n combined rows in four strata, interleaved so that
+    every prefix of the list is itself stratified: (1) the first and last main
+    rows of each sequence and of each contiguous run of query positions (the
+    chunks of a zigzag share); (2) the branch rows of anchors at sequence
+    starts and at the starts of those runs; (3) depth 1 and the deepest row of
+    the first and last anchor of each sequence and of random anchors; (4)
+    uniformly drawn rows."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    R = w.Nq + w.Rb
+    s1, s2, s3 = [], [], []
+    qp = w.q_pos.astype(np.int64)
+    for s in range(w.num_seqs):
+        lo, hi = int(w.cu_seqlens[s]), int(w.cu_seqlens[s + 1])
+        q0, q1 = (int(x) for x in np.searchsorted(qp, [lo, hi]))
+        run_starts = {lo}
+        if q1 > q0:
+            run = qp[q0:q1]
+            breaks = np.nonzero(np.diff(run) != 1)[0]
+            starts = np.concatenate([[0], breaks + 1])
+            ends = np.concatenate([breaks, [len(run) - 1]])
+            for a, b in zip(starts, ends):
+                s1 += [q0 + int(a), q0 + int(b)]
+                run_starts.add(int(run[a]))
+        m0, m1 = (int(x) for x in np.searchsorted(w.anchors, [lo, hi]))
+        for pos in sorted(run_starts):
+            m = int(np.searchsorted(w.anchors, pos))
+            if m < w.A and int(w.anchors[m]) == pos:
+                s2 += list(range(w.Nq + int(w.cu_branch[m]), w.Nq + int(w.cu_branch[m + 1])))
+        if m1 > m0:
+            for m in {m0, m1 - 1}:
+                b0, b1 = int(w.cu_branch[m]), int(w.cu_branch[m + 1])
+                if b1 > b0:
+                    s3 += [w.Nq + b0, w.Nq + b1 - 1]
+    if w.A:
+        for m in rng.integers(0, w.A, size=64):
+            b0, b1 = int(w.cu_branch[m]), int(w.cu_branch[m + 1])
+            if b1 > b0:
+                s3 += [w.Nq + b0, w.Nq + b1 - 1]
+    s4 = [int(x) for x in rng.integers(0, R, size=4 * n)]
+    strata = [list(dict.fromkeys(x)) for x in (s1, s2, s3, s4)]
+    out, seen, i = [], set(), 0
+    while len(out) < min(n, R) and any(i < len(x) for x in strata):
+        for x in strata:
+            if i < len(x) and x[i] not in seen and len(out) < n:
+                seen.add(x[i])
+                out.append(x[i])
+        i += 1
+    return out
+
+
+def cpu_info():
+    """Host facts recorded with the CPU baseline: core counts, CPU model and the
+    BLAS that numpy uses."""
+    import numpy as np
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = f"{b.get('name')} {b.get('version')}".strip()
+    except Exception:
+        pass
+    threads = 0
+    try:
+        from threadpoolctl import threadpool_info
+        for x in threadpool_info():
+            if x.get("user_api") == "blas":
+                threads = max(threads, int(x.get("num_threads", 0)))
+                blas = f"{blas} ({x.get('internal_api')}, {x.get('num_threads')} threads)"
+    except Exception:
+        pass
+    return {"affinity_cores": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count(),
+            "blas_threads": threads or None, "cpu_model": model, "blas": blas}
+
+
+def cpu_baseline(w, t, seconds, downscaled=()):
+    """The CPU oracle as it stands, timed on the machine's host cores: forward and
+    backward of a bounded prefix of a stratified 512-row sample of the same
+    workload (all heads), extrapolated to the whole problem by visible-pair
+    count; then, if given, the full dense oracle on downscaled versions of the
+    workloads."""
     import numpy as np
     import oracle
-    from workloads.inputs import to_f32
+    import workloads as W
+    from workloads.inputs import make_inputs, to_f32
 
     class View:
         def __init__(self, a):
@@ -165,33 +267,52 @@ def cpu_baseline(w, t, seconds):
         def __getitem__(self, i):
             return to_f32(self.a[i])
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([int(x.get("num_threads", 0)) for x in threadpool_info()] + [0])
-    except Exception:
-        cores = 0
-    cores = cores or len(os.sched_getaffinity(0))
+    info = cpu_info()
+    cores = info["blas_threads"] or info["affinity_cores"]
     p = oracle.Problem.from_workload(w)
     tv = {k: View(v) for k, v in t.items()}
     hm = oracle.branch_attention._HeadMajor(p, tv, np.float64)   # one-time layout copy, not timed
     acc = {"dk": np.zeros((w.N, w.num_kv_heads, w.head_dim)), "dv": np.zeros((w.N, w.num_kv_heads, w.head_dim)),
            "dkb": np.zeros((w.Rb, w.num_kv_heads, w.head_dim)), "dvb": np.zeros((w.Rb, w.num_kv_heads, w.head_dim))}
-    rng = np.random.default_rng(1234)
-    R = w.Nq + w.Rb
-    done, flops, t0 = [], 0, time.perf_counter()
-    while time.perf_counter() - t0 < seconds or len(done) < 2:
-        r = int(rng.integers(0, R))
+    sample = stratified_rows(w, 512)
+    done, t0 = [], time.perf_counter()
+    for r in sample:
+        if done and time.perf_counter() - t0 >= seconds:
+            break
         oracle.forward_rows(p, tv, [r], _hm=hm)
         oracle.backward_rows(p, tv, [r], acc, _hm=hm)
         done.append(r)
     el = time.perf_counter() - t0
     n_pairs = sum(row_pairs(w, done))
-    flops = n_pairs * w.num_q_heads * (4 + 10) * w.head_dim
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": (f"{len(done)} uniformly drawn rows (all {w.num_q_heads} heads) of {w.name}: fp64 numpy "
-                       f"forward + backward of each row over its visible keys ({n_pairs} row-key pairs), "
-                       f"{el:.1f} s; fwd+bwd flops counted as in value"),
-            "seconds": el}
+    full_pairs = sum(oracle.pair_counts(p).values())
+    fl = (4 + 10) * w.head_dim * w.num_q_heads
+    extrap_s = el * full_pairs / n_pairs
+    res = {"value": n_pairs * fl / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+           "sample": (f"first {len(done)} rows of a seeded stratified sample of 512 rows (sequence and chunk "
+                      f"ends, anchors at sequence starts, depth 1 and deepest branch rows, uniform rows) of "
+                      f"{w.name}, all {w.num_q_heads} heads: fp64 numpy forward + backward of each row over its "
+                      f"{n_pairs} visible row-key pairs in {el:.1f} s, extrapolated by pair count"),
+           "seconds": round(el, 2),
+           "extrapolated CPU time (%d cores)" % cores: round(extrap_s, 1),
+           "extrapolated_cpu_s": round(extrap_s, 1),
+           "rows_timed": len(done), "pairs_timed": n_pairs, "pairs_full": full_pairs,
+           "host": info, "downscaled": []}
+    for name in downscaled:
+        wd = W.get(name)
+        td = {k: to_f32(v).astype(np.float64) for k, v in make_inputs(wd, grads=True).items()}
+        pd = oracle.Problem.from_workload(wd)
+        t1 = time.perf_counter()
+        f = oracle.forward(pd, td)
+        t2 = time.perf_counter()
+        oracle.backward(pd, td, f)
+        t3 = time.perf_counter()
+        pairs = sum(oracle.pair_counts(pd).values())
+        res["downscaled"].append({"workload": wd.name, "fwd_s": round(t2 - t1, 2), "bwd_s": round(t3 - t2, 2),
+                                  "tflops": round((4 + 10) * wd.head_dim * wd.num_q_heads * pairs / (t3 - t1) / 1e12,
+                                                  5),
+                                  "what": "full dense fp64 oracle forward + backward"})
+        log(f"cpu downscaled {wd.name}: fwd {t2 - t1:.1f} s, bwd {t3 - t2:.1f} s")
+    return res
 
 
 def hbm_kernels(w, kern):
@@ -255,15 +376,20 @@ def ring_sim(sda, plan, g, w, stream, kern):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="ctx256k_rank3")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-downscaled", action="store_true",
+                    help="skip the full dense oracle on the downscaled workloads (part of the CPU baseline)")
+    ap.add_argument("--kernel-steps", type=int, default=2,
+                    help="steps of the separate pass, after the timed steps, that times each kernel launch "
+                         "with HIP events (per-kernel split and roofline)")
     ap.add_argument("--no-ring-sim", action="store_true",
                     help="skip the ring-step simulation measured after the timed steps")
     ap.add_argument("--no-clock", action="store_true",
-                    help="do not sample the shader clock (amd-smi) during the timed steps")
+                    help="do not sample the shader clock (sysfs) during the timed steps")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before the warmup, copy a buffer of this many MiB once (a plain copy kernel of known "
                          "size, for scaling hardware byte counters); not part of the timed region")
@@ -321,28 +447,41 @@ def main():
         step()
         torch.cuda.synchronize()
         log(f"warmup step {i} done")
-    sda.timing_reset()
-    sda.timing_enable(True)
+    # Timed region: exactly `steps` steps, one event between consecutive steps on
+    # the launch stream, the library's per-launch timing off.
+    props = torch.cuda.get_device_properties(dev)
+    pci = (props.pci_domain_id, props.pci_bus_id, props.pci_device_id) if hasattr(props, "pci_bus_id") else None
+    sda.timing_enable(False)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with ClockSampler(enabled=not args.no_clock) as clk:
-        e0.record(stream)
+    with ClockSampler(enabled=not args.no_clock, pci=pci) as clk:
+        ev[0].record(stream)
         for i in range(args.steps):
             step()
-        e1.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
-    sda.timing_enable(False)
     clock_mhz = clk.mhz()
-    ms = e0.elapsed_time(e1) / args.steps
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = float(np.median(per_step))
+    total_ms = ev[0].elapsed_time(ev[-1])
+    log(f"timed {args.steps} steps: median {ms:.1f} ms/step, total {total_ms:.1f} ms, clock {clock_mhz} MHz")
+    # Per-kernel split: a separate pass of the same steps with every launch
+    # bracketed by HIP events on the launch stream.
+    sda.timing_reset()
+    sda.timing_enable(True)
+    for i in range(max(1, args.kernel_steps)):
+        step()
+    torch.cuda.synchronize()
+    sda.timing_enable(False)
     kern = sda.timing_read()
-    log(f"timed {args.steps} steps: {ms:.1f} ms/step")
+    nks = max(1, args.kernel_steps)
 
     pairs = sum(plan.pairs)
     flops_fwd, flops_bwd = plan.flops_fwd(), plan.flops_bwd()
     value = (flops_fwd + flops_bwd) / (ms * 1e-3) / 1e12
     fwd_kernels = ("metadata_upload", "vt_transpose", "main_fwd", "branch_local_fwd", "lse_merge")
-    fwd_ms = sum(kern[k][0] for k in fwd_kernels if k in kern) / args.steps
-    bwd_ms = ms - fwd_ms
+    fwd_ms = sum(kern[k][0] for k in fwd_kernels if k in kern) / nks
+    bwd_ms = sum(v[0] for k, v in kern.items() if k not in fwd_kernels) / nks
     main_pairs = plan.pairs[0] + plan.pairs[1]
     # contraction flops each kernel must do per visible (row, key) pair and q head:
     # forward QK^T + PV (4d); dq kernel QK^T, dO V^T, dS K (6d); dkdv kernel
@@ -366,6 +505,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 3),
+        "ms_per_step_steps": [round(x, 3) for x in per_step],
+        "ms_total_timed": round(total_ms, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -376,6 +517,9 @@ def main():
                    "q_heads": hq, "kv_heads": w.num_kv_heads, "head_dim": d,
                    "description": w.description},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        # fwd_ms, bwd_ms and the per-kernel figures come from the separate
+        # kernel pass (kernel_steps steps, per-launch events)
+        "kernel_steps": nks,
         "fwd_ms": round(fwd_ms, 3),
         "bwd_ms": round(bwd_ms, 3),
         "fwd_tflops": round(flops_fwd / (fwd_ms * 1e-3) / 1e12, 2),
@@ -395,8 +539,11 @@ def main():
     if not args.no_ring_sim and w.name == "ctx256k_rank3":
         res["ring_sim"] = ring_sim(sda, plan, g, w, stream, kern)
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on sampled rows for ~{args.cpu_seconds:.0f} s")
-        res["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)
+        log(f"cpu baseline: oracle on stratified sampled rows for ~{args.cpu_seconds:.0f} s")
+        down = () if args.no_cpu_downscaled or w.name != "ctx256k_rank3" else ("ctx256k_rank3_chunk256",
+                                                                                 "qwen3_8b_16k_div16")
+        del g, gr, ws_f, ws_b, o, ob, lse, lseb
+        res["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds, down)
     print(json.dumps(res), flush=True)
 
 

@@ -35,6 +35,9 @@
  *     The library never allocates or frees device memory and never
  *     synchronizes a stream; the caller owns every buffer, including the
  *     workspace, and must keep them alive until the stream has run the work.
+ *   - Workspaces must be ordinary (coarse-grained) device memory, as from
+ *     hipMalloc or a torch CUDA tensor: the backward of plans with split key
+ *     tiles adds into the workspace with float32 atomics that assume it.
  *   - Errors are status codes; no C++ exception crosses this boundary. A
  *     non-OK status leaves a message for ba_last_error() (thread-local).
  *     NaN/Inf in the data are propagated, never checked.
@@ -130,6 +133,15 @@ ba_status_t branch_attn_fwd(const ba_plan_t *plan,
  * outputs (o, lse, ob, lseb) and the upstream gradients (d_o, d_ob). Every
  * gradient buffer is overwritten, not accumulated. The merge needs no backward
  * of its own: both parts are differentiated through the final LSE.
+ * Definition: the merged forward is one softmax over the union of each row's
+ * main-prefix and branch keys (rcap.io explainer, paragraph on branch attention
+ * under context parallelism: the two partials are joined by the same
+ * log-sum-exp step ring attention uses, leaving the numerics unchanged; evolve.pub
+ * review, "Scope & Claims", section 3.2 and Eq. 2). The pages print no
+ * backward; this is the exact gradient of that softmax:
+ *   P = exp(S - LSE), D = rowsum(dO * O), dS = P * (dO V^T - D),
+ *   dQ = scale dS K, dK = scale dS^T Q and dV = P^T dO summed over the q heads
+ *   of each kv head, for main and branch keys alike.
  * workspace: ws_bytes >= ba_workspace_bytes(plan, 1). */
 ba_status_t branch_attn_bwd(const ba_plan_t *plan,
                             const void *q, const void *k, const void *v,
@@ -155,6 +167,12 @@ ba_status_t lse_merge(int64_t rows, int32_t heads, int32_t head_dim,
 /* Split path, the pieces branch_attn_fwd chains (exposed for tests and for
  * callers that merge elsewhere). Both upload the plan metadata into the
  * workspace (ws_bytes >= ba_workspace_bytes(plan, 2)).
+ * The split is the paper's decomposition: a main-sequence part over the packed
+ * causal prefix that emits output plus log-sum-exp, and a branch-local part
+ * against K/V that never leave the branch's anchor, joined by Eq. 2 (evolve.pub
+ * review, "Scope & Claims", section 3.2 and Eq. 2, and "Frequently asked
+ * questions" on branch attention under context parallelism; rcap.io explainer,
+ * paragraph on branch attention under context parallelism).
  * ba_main_fwd: every row against its causal main prefix: final o/lse for main
  * rows, float32 partial o_pre [Rb,Hq,d] / lse_pre [Hq,Rb] for branch rows.
  * ba_branch_local_fwd: branch rows against their own branch keys only:

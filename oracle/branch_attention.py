@@ -20,9 +20,9 @@ Which keys a row sees (the mask)
   branch, all of them for a block -- (rcap.io explainer, paragraph on branch
   attention under context parallelism: a branch query sees the causal prefix
   of the main sequence plus a small set of branch-local keys);
-* main rows never see branch keys: branches hang off the main sequence rather
-  than continuing it (cere-bro wiki, "Mechanism", paragraph on context
-  parallelism).
+* main rows never see branch keys: a branch forks from its anchor and is never
+  part of the main sequence, so no main query can reach it (cere-bro wiki,
+  "Mechanism", paragraph on context parallelism).
 
 Per head h (kv head g = kv_head_of[h]) over the row's visible keys:
   S = scale * q.k,  LSE = log(sum(exp(S))),  P = exp(S - LSE),  O = P V.
@@ -61,6 +61,10 @@ class Problem:
 
     @classmethod
     def from_workload(cls, w, kv_head_of=None, scale=None) -> "Problem":
+        if kv_head_of is None:
+            kv_head_of = getattr(w, "kv_head_of", None)
+        if scale is None:
+            scale = getattr(w, "softmax_scale", None) or None
         return cls(w.num_q_heads, w.num_kv_heads, w.head_dim, w.cu_seqlens, w.q_pos, w.anchors,
                    w.cu_branch, w.modes, kv_head_of, scale)
 

@@ -185,7 +185,12 @@ class Plan:
         self.pairs = tuple(int(x) for x in pairs)
 
     @classmethod
-    def from_workload(cls, w, softmax_scale: float = 0.0, kv_head_of=None) -> "Plan":
+    def from_workload(cls, w, softmax_scale: Optional[float] = None, kv_head_of=None) -> "Plan":
+        """Plan of a workload description; its own head map and scale unless overridden."""
+        if softmax_scale is None:
+            softmax_scale = getattr(w, "softmax_scale", 0.0) or 0.0
+        if kv_head_of is None:
+            kv_head_of = getattr(w, "kv_head_of", None)
         return cls(BA_BF16 if w.dtype == "bf16" else BA_F32, w.num_q_heads, w.num_kv_heads, w.head_dim,
                    w.cu_seqlens, w.q_pos, w.anchors, w.cu_branch, w.modes, softmax_scale=softmax_scale,
                    kv_head_of=kv_head_of)

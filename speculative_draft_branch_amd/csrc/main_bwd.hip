@@ -7,7 +7,10 @@
 // Eq. 2; the merged result is one softmax over the union of keys, rcap.io
 // explainer, paragraph on branch attention under context parallelism.)
 //
-// Two kernels, no atomics:
+// Two kernels. Every gradient element has one writer, except in plans whose
+// backward key tiles are split (small plans only): there each dK/dV element
+// gets one or two float32 atomic adds into a zeroed accumulator, a sum of at
+// most two terms, so the result does not depend on their order.
 //  * dq: query-tile major, the forward's work unit (query tile x its key range,
 //    64-key LDS tiles). S^T = K Q^T and dP^T = V dO^T put one query row on each
 //    lane (dP^T starts from -D of that row); dQ^T += K^T dS^T takes K through

@@ -49,7 +49,8 @@ def visible_keys(cu, q_pos, anchors, cu_branch, modes, row):
 
 def brute_forward(cu, q_pos, anchors, cu_branch, modes, q, k, v, qb, kb, vb, kv_group, scale):
     """Returns per combined row, per head: (O list, LSE float). Tensors are nested
-    lists or arrays indexable as x[row][head][dim]."""
+    lists or arrays indexable as x[row][head][dim]. ``kv_group``: the group size G
+    (q head h reads kv head h // G) or an explicit list, entry h = kv head of q head h."""
     nq = len(q_pos)
     rows = nq + int(cu_branch[-1])
     hq = len(q[0]) if nq else len(qb[0])
@@ -60,7 +61,7 @@ def brute_forward(cu, q_pos, anchors, cu_branch, modes, q, k, v, qb, kb, vb, kv_
         qrow = q[r] if r < nq else qb[r - nq]
         per_head = []
         for h in range(hq):
-            g = h // kv_group
+            g = h // kv_group if isinstance(kv_group, int) else int(kv_group[h])
             scores, vals = [], []
             for kind, idx in keys:
                 kk = k[idx][g] if kind == "main" else kb[idx][g]

@@ -21,20 +21,73 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
 
 
-def test_clock_sampler_off_when_disabled_or_under_a_profiler(monkeypatch):
-    monkeypatch.delenv("LD_PRELOAD", raising=False)
-    monkeypatch.delenv("HSA_TOOLS_LIB", raising=False)
-    assert bench.ClockSampler(enabled=False).tool is None
-    # a preloaded profiler library would initialise the GPU inside the tool's
-    # process before it execs its interpreter: the sampler must not start it
-    monkeypatch.setenv("LD_PRELOAD", "/opt/rocm/lib/rocprofiler-sdk/librocprofiler-sdk-tool.so")
-    assert bench.ClockSampler().tool is None
-    monkeypatch.delenv("LD_PRELOAD")
-    monkeypatch.setenv("HSA_TOOLS_LIB", "librocprofiler64.so")
-    assert bench.ClockSampler().tool is None
+def test_clock_sampler_reads_sysfs_and_starts_no_tool(tmp_path, monkeypatch):
+    """The clock comes from the pp_dpm_sclk text in this process (no subprocess,
+    so nothing is exec'd from a process that may have touched the GPU)."""
+    txt = "0: 500Mhz\n1: 1843Mhz *\n2: 2400Mhz\n"
+    assert bench.parse_sclk(txt) == 1843.0
+    assert bench.parse_sclk("0: 500Mhz\n1: 2400Mhz\n") is None
+    assert bench.parse_sclk("") is None
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text(txt)
+    import subprocess as sp
+
+    def no_subprocess(*a, **k):
+        raise AssertionError("the clock sampler must not start a process")
+
+    monkeypatch.setattr(sp, "run", no_subprocess)
+    monkeypatch.setattr(sp, "Popen", no_subprocess)
+    monkeypatch.setattr(bench, "_sclk_path", lambda pci=None: str(f))
+    with bench.ClockSampler() as clk:
+        import time
+        time.sleep(0.3)
+    assert clk.mhz() == 1843.0
     with bench.ClockSampler(enabled=False) as clk:
         pass
-    assert clk.mhz() is None
+    assert clk.path is None and clk.mhz() is None
+
+
+def test_clock_path_of_a_missing_device_is_none():
+    assert bench._sclk_path((0xffff, 0xff, 0x1f)) is None
+
+
+def test_stratified_sample_covers_each_stratum():
+    import numpy as np
+    import workloads as W
+    w = W.get("ctx256k_rank3")
+    rows = bench.stratified_rows(w, 512)
+    assert len(rows) == 512 == len(set(rows))
+    assert all(0 <= r < w.Nq + w.Rb for r in rows)
+    c = 16384
+    # first and last rows of both query chunks (chunks 3 and 12), early in the list
+    head = set(rows[:40])
+    assert {0, c - 1, c, 2 * c - 1} <= head
+    # branch rows of the anchors at the chunk starts (positions 3c and 12c)
+    assert w.Nq + 0 in rows and w.Nq + 7 * c in rows
+    # depth 1 and depth 7 rows
+    depth = [(r - w.Nq) % 7 for r in rows if r >= w.Nq]
+    assert 0 in depth and 6 in depth
+    # packed sequences: first and last row of every sequence
+    w2 = W.get("qwen3_8b_16k")
+    rows2 = set(bench.stratified_rows(w2, 512))
+    for s in range(w2.num_seqs):
+        assert int(w2.cu_seqlens[s]) in rows2 and int(w2.cu_seqlens[s + 1]) - 1 in rows2
+    # deterministic
+    assert bench.stratified_rows(w, 512) == rows
+    del np
+
+
+def test_cpu_baseline_extrapolates_by_pair_count():
+    import workloads as W
+    from workloads.inputs import make_inputs
+    w = W.get("ctx256k_rank3_chunk64")
+    t = make_inputs(w, grads=True)
+    r = bench.cpu_baseline(w, t, 0.5)
+    assert r["kind"] == "oracle" and r["cores"] >= 1 and r["rows_timed"] >= 1
+    assert r["pairs_timed"] == sum(bench.row_pairs(w, bench.stratified_rows(w, 512)[:r["rows_timed"]]))
+    key = "extrapolated CPU time (%d cores)" % r["cores"]
+    assert abs(r[key] - r["seconds"] * r["pairs_full"] / r["pairs_timed"]) <= 0.1 + 1e-3 * r[key]
+    assert r["host"]["os_cpu_count"] == os.cpu_count()
 
 
 def test_kernel_source_hash_ignores_comment_only_edits(tmp_path, monkeypatch):

@@ -117,6 +117,91 @@ def test_forward_matches_brute_force(name):
             assert abs(gl - lse) < 1e-12
 
 
+# Explicit GQA head maps and a softmax scale other than 1/sqrt(d): q head h reads
+# kv head kv_head_of[h]. Group sizes 3 and 5 (not powers of two), a strided map,
+# a seeded permutation.
+HEADMAP_CASES = {
+    "strided_g3": dict(hq=6, hkv=2, kv_head_of=[0, 1, 0, 1, 0, 1], scale=0.37),
+    "perm_g5": dict(hq=10, hkv=2, kv_head_of=[1, 0, 0, 1, 1, 0, 1, 0, 0, 1], scale=None),
+    "contig_g3_scale": dict(hq=3, hkv=1, kv_head_of=None, scale=1.9),
+}
+
+
+def _headmap_case(name):
+    c = HEADMAP_CASES[name]
+    w = _tiny(name, hq=c["hq"], hkv=c["hkv"], d=8)
+    w.kv_head_of = None if c["kv_head_of"] is None else np.asarray(c["kv_head_of"], np.int32)
+    w.softmax_scale = c["scale"] or 0.0
+    return w
+
+
+@pytest.mark.parametrize("name", list(HEADMAP_CASES))
+def test_forward_with_head_map_and_scale_matches_brute_force(name):
+    w = _headmap_case(name)
+    p = Problem.from_workload(w)
+    c = HEADMAP_CASES[name]
+    scale = c["scale"] or 1.0 / math.sqrt(w.head_dim)
+    assert p.scale == scale
+    kvmap = c["kv_head_of"] if c["kv_head_of"] is not None else w.num_q_heads // w.num_kv_heads
+    t = _f64(make_inputs(w))
+    f = oracle.forward(p, t)
+    bf = brute_force.brute_forward(w.cu_seqlens, w.q_pos, w.anchors, w.cu_branch, w.modes,
+                                   t["q"], t["k"], t["v"], t["qb"], t["kb"], t["vb"], kvmap, scale)
+    for r, per_head in enumerate(bf):
+        for h, (o, lse) in enumerate(per_head):
+            if r < p.Nq:
+                go, gl = f["o"][r, h], f["lse"][h, r]
+            else:
+                go, gl = f["ob"][r - p.Nq, h], f["lseb"][h, r - p.Nq]
+            np.testing.assert_allclose(go, o, rtol=0, atol=1e-12)
+            assert abs(gl - lse) < 1e-12
+
+
+@pytest.mark.parametrize("name", list(HEADMAP_CASES))
+def test_backward_with_head_map_and_scale_matches_autograd(name):
+    """fp64 autograd of masked softmax attention, K/V expanded per q head by the map."""
+    w = _headmap_case(name)
+    p = Problem.from_workload(w)
+    t = _f64(make_inputs(w, grads=True))
+    g = oracle.backward(p, t, oracle.forward(p, t))
+    mask = torch.from_numpy(oracle.dense_mask(p))
+    Q = torch.tensor(np.concatenate([t["q"], t["qb"]]), requires_grad=True)
+    K = torch.tensor(np.concatenate([t["k"], t["kb"]]), requires_grad=True)
+    V = torch.tensor(np.concatenate([t["v"], t["vb"]]), requires_grad=True)
+    dO = torch.tensor(np.concatenate([t["do"], t["dob"]]))
+    c = HEADMAP_CASES[name]
+    idx = torch.tensor(c["kv_head_of"] if c["kv_head_of"] is not None
+                       else [h // (p.hq // p.hkv) for h in range(p.hq)])
+    scale = c["scale"] or 1.0 / math.sqrt(w.head_dim)
+    Ke, Ve = K.index_select(1, idx), V.index_select(1, idx)
+    S = torch.einsum("rhd,khd->hrk", Q, Ke) * scale
+    S = S.masked_fill(~mask, float("-inf"))
+    O = torch.einsum("hrk,khd->rhd", torch.softmax(S, dim=-1), Ve)
+    (O * dO).sum().backward()
+    nq, n = p.Nq, p.N
+    for got, ref in ((g["dq"], Q.grad[:nq]), (g["dqb"], Q.grad[nq:]), (g["dk"], K.grad[:n]),
+                     (g["dkb"], K.grad[n:]), (g["dv"], V.grad[:n]), (g["dvb"], V.grad[n:])):
+        np.testing.assert_allclose(got, ref.numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("name", list(HEADMAP_CASES))
+def test_row_restricted_with_head_map_matches_dense(name):
+    w = _headmap_case(name)
+    p = Problem.from_workload(w)
+    t = _f64(make_inputs(w, grads=True))
+    f = oracle.forward(p, t)
+    g = oracle.backward(p, t, f)
+    rows = list(range(p.Nq + p.Rb))
+    O, L = oracle.forward_rows(p, t, rows)
+    np.testing.assert_allclose(O, np.concatenate([f["o"], f["ob"]]), atol=1e-12)
+    np.testing.assert_allclose(L, np.concatenate([f["lse"], f["lseb"]], axis=1), atol=1e-12)
+    acc = {k: np.zeros_like(t[k[1:]]) for k in ("dk", "dv", "dkb", "dvb")}
+    dQ = oracle.backward_rows(p, t, rows, acc)
+    np.testing.assert_allclose(dQ, np.concatenate([g["dq"], g["dqb"]]), atol=1e-12)
+    for k in acc:
+        np.testing.assert_allclose(acc[k], g[k], atol=1e-12)
+
+
 def _expand_kv(x, hq):
     """[K, Hkv, d] -> [Hq, K, d] with contiguous GQA groups."""
     rep = hq // x.shape[1]

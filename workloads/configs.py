@@ -45,6 +45,8 @@ class Workload:
     seed: int = 0
     passes: tuple = ("fwd",)
     description: str = ""
+    kv_head_of: Optional[np.ndarray] = None  # int32 [Hq] kv head of each q head; None -> h // (Hq/Hkv)
+    softmax_scale: float = 0.0               # 0 -> 1/sqrt(head_dim)
 
     @property
     def N(self) -> int:
@@ -193,6 +195,7 @@ _REGISTRY: Dict[str, Callable[[], Workload]] = {
     "qwen3_8b_16k_div16": lambda: qwen3_8b_16k(16),
     "dflash_64k_1024": lambda: dflash_64k(1024),
     "ctx256k_rank3_chunk64": lambda: ctx256k_rank3(64),
+    "ctx256k_rank3_chunk256": lambda: ctx256k_rank3(256),
     "ctx256k_rank3_chunk80": lambda: ctx256k_rank3(80),
     "gptoss_128k_mixed_2048": lambda: gptoss_128k_mixed(2048, 32, 512, 0),
 }
