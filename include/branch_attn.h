@@ -129,6 +129,23 @@ ba_status_t branch_attn_fwd(const ba_plan_t *plan,
                             void *o, float *lse, void *ob, float *lseb,
                             void *workspace, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): branch_attn_fwd without a
+ * workspace argument. Its scratch (plan metadata, transposed V tiles and the
+ * float32 main-prefix partial of the branch rows) lives in a fixed array of
+ * ba_fwd_noalloc_max_bytes() = 64 MiB of device memory per GPU, which the
+ * library holds from its first use on that GPU until the process ends; the
+ * call allocates and frees nothing. Problems whose ba_workspace_bytes(plan, 0)
+ * exceeds that size return BA_EWORKSPACE without enqueuing work. Every call on
+ * one GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race, so serialize them.
+ * Results are identical to branch_attn_fwd's. Arguments as branch_attn_fwd. */
+ba_status_t branch_attn_fwd_noalloc(const ba_plan_t *plan,
+                                    const void *q, const void *k, const void *v,
+                                    const void *qb, const void *kb, const void *vb,
+                                    void *o, float *lse, void *ob, float *lseb, void *stream);
+size_t ba_fwd_noalloc_max_bytes(void);
+
 /* Backward pass: exact gradients of the merged forward, given the forward's
  * outputs (o, lse, ob, lseb) and the upstream gradients (d_o, d_ob). Every
  * gradient buffer is overwritten, not accumulated. The merge needs no backward

@@ -15,6 +15,6 @@ from ._abi import (  # noqa: F401
     timing_read,
 )
 from .ops import (  # noqa: F401
-    branch_attn_fwd, branch_attn_bwd, lse_merge, ba_main_fwd, ba_branch_local_fwd, ba_ring_step_fwd, fwd, bwd,
+    branch_attn_fwd, branch_attn_fwd_noalloc, fwd_noalloc_max_bytes, branch_attn_bwd, lse_merge, ba_main_fwd, ba_branch_local_fwd, ba_ring_step_fwd, fwd, bwd,
     workspace,
 )

@@ -65,6 +65,10 @@ def _load():
     L.ba_plan_pairs.restype = st
     L.branch_attn_fwd.argtypes = [vp] + [vp] * 6 + [vp, vp, vp, vp] + [vp, sz, vp]
     L.branch_attn_fwd.restype = st
+    L.branch_attn_fwd_noalloc.argtypes = [vp] + [vp] * 6 + [vp, vp, vp, vp] + [vp]
+    L.branch_attn_fwd_noalloc.restype = st
+    L.ba_fwd_noalloc_max_bytes.argtypes = []
+    L.ba_fwd_noalloc_max_bytes.restype = sz
     L.branch_attn_bwd.argtypes = [vp] + [vp] * 6 + [vp, vp, vp, vp] + [vp, vp] + [vp] * 6 + [vp, sz, vp]
     L.branch_attn_bwd.restype = st
     L.lse_merge.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, C.c_int, vp, vp]
@@ -103,7 +107,7 @@ def abi_version() -> int:
 
 def exported_symbols() -> list:
     return ["ba_plan_create", "ba_plan_destroy", "ba_workspace_bytes", "ba_plan_sizes", "ba_plan_pairs",
-            "branch_attn_fwd", "branch_attn_bwd", "lse_merge", "ba_main_fwd", "ba_branch_local_fwd",
+            "branch_attn_fwd", "branch_attn_fwd_noalloc", "ba_fwd_noalloc_max_bytes", "branch_attn_bwd", "lse_merge", "ba_main_fwd", "ba_branch_local_fwd",
             "ba_ring_step_fwd",
             "ba_status_str", "ba_last_error", "ba_abi_version", "ba_timing_enable", "ba_timing_reset",
             "ba_timing_kernels", "ba_timing_kernel_name", "ba_timing_read"]

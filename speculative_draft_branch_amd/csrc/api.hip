@@ -190,6 +190,76 @@ ba_status_t check_plan(const ba_plan *pl) {
   return BA_OK;
 }
 
+// Scratch of the allocation-free forward: one array per device, held for the
+// life of the process. Host code never passes the array's name to a kernel
+// (on the host that name is a stand-in, not a device address); it passes the
+// address hipGetSymbolAddress returns, once per device, with that device
+// current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+ba_status_t scratch_of_current_device(void **out) {
+  int dev = -1;
+  BA_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return set_error(BA_EUNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    BA_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p || reinterpret_cast<uintptr_t>(p) % 256 != 0)
+      return set_error(BA_EHIP, "scratch address is NULL or not 256-byte aligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BA_OK;
+}
+
+// The forward pass after argument checks: workspace of at least
+// ba_workspace_bytes(plan, 0) bytes.
+ba_status_t fwd_body(const ba_plan *pl, const void *q, const void *k, const void *v, const void *qb, const void *kb,
+                     const void *vb, void *o, float *lse, void *ob, float *lseb, void *workspace, hipStream_t st) {
+  BA_TRY(upload(pl, workspace, st));
+  const Meta mt = make_meta(pl, workspace);
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  float *o_pre = reinterpret_cast<float *>(ws + pl->off_o_pre);
+  float *lse_pre = reinterpret_cast<float *>(ws + pl->off_lse_pre);
+  BA_TRY(run_main_fwd(pl, mt, q, qb, k, v, o, lse, o_pre, lse_pre, workspace, st));
+  if (pl->dtype == BA_BF16)  // branch-local attention and the merge in one kernel
+    return timed(K_BRANCH_LOCAL_FWD, st, "branch-local forward + merge", [&] {
+      return launch_branch_fwd_bf16(mt, (const bf16 *)qb, (const bf16 *)kb, (const bf16 *)vb, o_pre, lse_pre, nullptr,
+                                    nullptr, (bf16 *)ob, lseb, st);
+    });
+  float *o_loc = reinterpret_cast<float *>(ws + pl->off_o_loc);
+  float *lse_loc = reinterpret_cast<float *>(ws + pl->off_lse_loc);
+  BA_TRY(timed(K_BRANCH_LOCAL_FWD, st, "branch-local forward",
+               [&] { return launch_branch_local_fwd(mt, pl->dtype, qb, kb, vb, o_loc, lse_loc, st); }));
+  BA_TRY(timed(K_LSE_MERGE, st, "lse_merge", [&] {
+    return launch_lse_merge(pl->Rb, pl->hq, pl->d, o_pre, lse_pre, o_loc, lse_loc, ob, pl->dtype, lseb, st);
+  }));
+  return BA_OK;
+}
+
+ba_status_t check_fwd_args(const ba_plan *pl, const void *q, const void *k, const void *v, const void *qb,
+                           const void *kb, const void *vb, const void *o, const float *lse, const void *ob,
+                           const float *lseb) {
+  BA_TRY(check_plan(pl));
+  const int64_t hd = (int64_t)pl->hq * pl->d, kd = (int64_t)pl->hkv * pl->d;
+  BA_TRY(check_ptr(q, pl->Nq * hd, "q"));
+  BA_TRY(check_ptr(k, pl->N * kd, "k"));
+  BA_TRY(check_ptr(v, pl->N * kd, "v"));
+  BA_TRY(check_ptr(qb, pl->Rb * hd, "qb"));
+  BA_TRY(check_ptr(kb, pl->Rb * kd, "kb"));
+  BA_TRY(check_ptr(vb, pl->Rb * kd, "vb"));
+  BA_TRY(check_ptr(o, pl->Nq * hd, "o"));
+  BA_TRY(check_ptr(lse, pl->Nq * pl->hq, "lse"));
+  BA_TRY(check_ptr(ob, pl->Rb * hd, "ob"));
+  BA_TRY(check_ptr(lseb, pl->Rb * pl->hq, "lseb"));
+  return BA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -284,39 +354,25 @@ ba_status_t lse_merge(int64_t rows, int32_t heads, int32_t head_dim, const float
 ba_status_t branch_attn_fwd(const ba_plan_t *pl, const void *q, const void *k, const void *v, const void *qb,
                             const void *kb, const void *vb, void *o, float *lse, void *ob, float *lseb,
                             void *workspace, size_t ws_bytes, void *stream) {
-  BA_TRY(check_plan(pl));
-  const int64_t hd = (int64_t)pl->hq * pl->d, kd = (int64_t)pl->hkv * pl->d;
-  BA_TRY(check_ptr(q, pl->Nq * hd, "q"));
-  BA_TRY(check_ptr(k, pl->N * kd, "k"));
-  BA_TRY(check_ptr(v, pl->N * kd, "v"));
-  BA_TRY(check_ptr(qb, pl->Rb * hd, "qb"));
-  BA_TRY(check_ptr(kb, pl->Rb * kd, "kb"));
-  BA_TRY(check_ptr(vb, pl->Rb * kd, "vb"));
-  BA_TRY(check_ptr(o, pl->Nq * hd, "o"));
-  BA_TRY(check_ptr(lse, pl->Nq * pl->hq, "lse"));
-  BA_TRY(check_ptr(ob, pl->Rb * hd, "ob"));
-  BA_TRY(check_ptr(lseb, pl->Rb * pl->hq, "lseb"));
+  BA_TRY(check_fwd_args(pl, q, k, v, qb, kb, vb, o, lse, ob, lseb));
   BA_TRY(check_ws(pl, workspace, ws_bytes, 0));
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  BA_TRY(upload(pl, workspace, st));
-  const Meta mt = make_meta(pl, workspace);
-  uint8_t *ws = static_cast<uint8_t *>(workspace);
-  float *o_pre = reinterpret_cast<float *>(ws + pl->off_o_pre);
-  float *lse_pre = reinterpret_cast<float *>(ws + pl->off_lse_pre);
-  BA_TRY(run_main_fwd(pl, mt, q, qb, k, v, o, lse, o_pre, lse_pre, workspace, st));
-  if (pl->dtype == BA_BF16)  // branch-local attention and the merge in one kernel
-    return timed(K_BRANCH_LOCAL_FWD, st, "branch-local forward + merge", [&] {
-      return launch_branch_fwd_bf16(mt, (const bf16 *)qb, (const bf16 *)kb, (const bf16 *)vb, o_pre, lse_pre, nullptr,
-                                    nullptr, (bf16 *)ob, lseb, st);
-    });
-  float *o_loc = reinterpret_cast<float *>(ws + pl->off_o_loc);
-  float *lse_loc = reinterpret_cast<float *>(ws + pl->off_lse_loc);
-  BA_TRY(timed(K_BRANCH_LOCAL_FWD, st, "branch-local forward",
-               [&] { return launch_branch_local_fwd(mt, pl->dtype, qb, kb, vb, o_loc, lse_loc, st); }));
-  BA_TRY(timed(K_LSE_MERGE, st, "lse_merge", [&] {
-    return launch_lse_merge(pl->Rb, pl->hq, pl->d, o_pre, lse_pre, o_loc, lse_loc, ob, pl->dtype, lseb, st);
-  }));
-  return BA_OK;
+  return fwd_body(pl, q, k, v, qb, kb, vb, o, lse, ob, lseb, workspace, static_cast<hipStream_t>(stream));
+}
+
+size_t ba_fwd_noalloc_max_bytes(void) { return kScratchBytes; }
+
+ba_status_t branch_attn_fwd_noalloc(const ba_plan_t *pl, const void *q, const void *k, const void *v, const void *qb,
+                                    const void *kb, const void *vb, void *o, float *lse, void *ob, float *lseb,
+                                    void *stream) {
+  BA_TRY(check_fwd_args(pl, q, k, v, qb, kb, vb, o, lse, ob, lseb));
+  const size_t need = ba_workspace_bytes(pl, 0);
+  if (need > kScratchBytes)
+    return set_error(BA_EWORKSPACE, "branch_attn_fwd_noalloc: the problem needs " + std::to_string(need) +
+                                        " bytes of scratch, more than its fixed " + std::to_string(kScratchBytes) +
+                                        " bytes; use branch_attn_fwd with a workspace");
+  void *ws = nullptr;
+  BA_TRY(scratch_of_current_device(&ws));
+  return fwd_body(pl, q, k, v, qb, kb, vb, o, lse, ob, lseb, ws, static_cast<hipStream_t>(stream));
 }
 
 ba_status_t branch_attn_bwd(const ba_plan_t *pl, const void *q, const void *k, const void *v, const void *qb,

@@ -54,6 +54,22 @@ def branch_attn_fwd(plan: Plan, q, k, v, qb, kb, vb, o, lse, ob, lseb, ws: torch
                               _p(lseb), _p(ws), ws.numel(), _stream()), "branch_attn_fwd")
 
 
+def branch_attn_fwd_noalloc(plan: Plan, q, k, v, qb, kb, vb, o, lse, ob, lseb):
+    """branch_attn_fwd on the library's fixed per-GPU scratch: no workspace, no allocation."""
+    dt, s = _DT[plan.dtype], _shapes(plan)
+    for t, n, key in ((q, "q", "q"), (k, "k", "k"), (v, "v", "k"), (qb, "qb", "qb"), (kb, "kb", "kb"),
+                      (vb, "vb", "kb"), (o, "o", "q"), (ob, "ob", "qb")):
+        _chk(t, n, dt, s[key])
+    _chk(lse, "lse", torch.float32, s["lse"])
+    _chk(lseb, "lseb", torch.float32, s["lseb"])
+    check(lib.branch_attn_fwd_noalloc(plan.handle, _p(q), _p(k), _p(v), _p(qb), _p(kb), _p(vb), _p(o), _p(lse),
+                                      _p(ob), _p(lseb), _stream()), "branch_attn_fwd_noalloc")
+
+
+def fwd_noalloc_max_bytes() -> int:
+    return int(lib.ba_fwd_noalloc_max_bytes())
+
+
 def branch_attn_bwd(plan: Plan, q, k, v, qb, kb, vb, o, lse, ob, lseb, do, dob, dq, dk, dv, dqb, dkb, dvb,
                     ws: torch.Tensor):
     dt, s = _DT[plan.dtype], _shapes(plan)

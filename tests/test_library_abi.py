@@ -16,22 +16,23 @@ from speculative_draft_branch_amd import Plan, BranchAttnError, BA_EINVAL, BA_EU
 
 import oracle
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "branch_attn.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
 
 
 def _declared_functions():
-    text = open(HEADER).read()
+    text = open(os.path.join(INCLUDE, "branch_attn.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\(", text)
     skip = {"if", "sizeof", "defined", "extern", "typedef"}
-    return sorted({n for n in names if n not in skip and (n.startswith("ba_") or n in (
-        "branch_attn_fwd", "branch_attn_bwd", "lse_merge"))})
+    return sorted({n for n in names if n not in skip and (n.startswith(("ba_", "branch_attn_")) or n in (
+        "lse_merge",))})
 
 
 def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(sda.library_path())
     declared = _declared_functions()
     assert "branch_attn_fwd" in declared and "lse_merge" in declared and "ba_plan_create" in declared
+    assert "branch_attn_fwd_noalloc" in declared
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(sda.exported_symbols())
