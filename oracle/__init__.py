@@ -21,6 +21,11 @@ context-parallel ring delivers them).
 
 Arithmetic is float64 unless a caller asks otherwise.
 
+``oracle.tapchannel`` is a plain model of the tap mailbox (slots with sequence
+stamps, one-way writes and reads; rcap.io explainer, the TapChannel paragraph),
+pinned in ``tests/test_tapchannel_host.py`` by every interleaving of a small
+writer and reader and by a hand-worked script.
+
 Readings adopted where the pages are silent (each is also a test):
   * softmax scale 1/sqrt(head_dim); LSE is the natural log of sum(exp(scale*q.k));
   * a branch row sees main keys from its sequence start to its anchor,
