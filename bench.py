@@ -316,14 +316,16 @@ def cpu_baseline(w, t, seconds, downscaled=()):
 
 
 def hbm_kernels(w, kern):
-    """Branch-local kernels (bf16): algorithmic HBM bytes per launch and the rate
-    against the 8 TB/s peak. Forward, per (branch row, q head): Q 2d, the main
-    partial 4d + 4 in, the merged output 2d + 4 out; per (branch row, kv head):
-    K, V 4d. Backward, per (branch row, q head): Q, dO 4d, the dQ accumulator 4d
-    in, dQ 2d out, LSE and D 8; per (branch row, kv head): K, V in and dK, dV out 8d."""
+    """HBM-bound kernels (bf16): algorithmic bytes per launch and the rate
+    against the 8 TB/s peak. Branch-local backward (dK, dV of the branch keys),
+    per (branch row, q head): Q, dO 4d, LSE and D 8; per (branch row, kv head):
+    K, V in and dK, dV out 8d. Backward gather, per (row, q head): Q, O, dO read
+    and the scaled Q and dO written, 10d, plus LSE, D in and the staged pair and
+    D out, 16."""
     rb, hq, hkv, d = w.Rb, w.num_q_heads, w.num_kv_heads, w.head_dim
-    byt = {"branch_local_fwd": rb * hq * (8 * d + 8) + rb * hkv * 4 * d,
-           "branch_local_bwd": rb * hq * (10 * d + 8) + rb * hkv * 8 * d}
+    rows = w.Nq + w.Rb
+    byt = {"branch_local_bwd": rb * hq * (4 * d + 8) + rb * hkv * 8 * d,
+           "bwd_preprocess": rows * hq * (10 * d + 16)}
     out = {}
     for k, b in byt.items():
         if k in kern and kern[k][1]:
@@ -479,7 +481,7 @@ def main():
     pairs = sum(plan.pairs)
     flops_fwd, flops_bwd = plan.flops_fwd(), plan.flops_bwd()
     value = (flops_fwd + flops_bwd) / (ms * 1e-3) / 1e12
-    fwd_kernels = ("metadata_upload", "vt_transpose", "main_fwd", "branch_local_fwd", "lse_merge")
+    fwd_kernels = ("metadata_upload", "vt_transpose", "vbt_transpose", "main_fwd", "branch_local_fwd", "lse_merge")
     fwd_ms = sum(kern[k][0] for k in fwd_kernels if k in kern) / nks
     bwd_ms = sum(v[0] for k, v in kern.items() if k not in fwd_kernels) / nks
     main_pairs = plan.pairs[0] + plan.pairs[1]

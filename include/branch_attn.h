@@ -119,10 +119,14 @@ ba_status_t ba_plan_sizes(const ba_plan_t *plan, int64_t out[5]);
 ba_status_t ba_plan_pairs(const ba_plan_t *plan, int64_t out[3]);
 
 /* Forward pass: o/lse for main rows, ob/lseb for branch rows (merged result).
- * Enqueues: metadata upload into the workspace, the main-sequence kernel (all
- * rows against their causal main prefix), the branch-local kernel and the
- * log-sum-exp merge; for BA_BF16 the merge runs inside the branch-local kernel
- * (no float32 branch-local partial in HBM). workspace: device buffer of ws_bytes >= ba_workspace_bytes(plan, 0). */
+ * BA_BF16: the metadata upload, the transposes of V and of the branch V, and
+ * one kernel in which every row attends its causal main prefix and then, as
+ * the last key tiles of the same online softmax, its own branch's keys, so the
+ * log-sum-exp merge of the two parts happens inside that pass (cere-bro wiki,
+ * "Mechanism": the branch part rides in the same ring pass) and no partial
+ * reaches HBM. BA_F32: the main-sequence kernel (float32 partial for branch
+ * rows), the branch-local kernel and lse_merge.
+ * workspace: device buffer of ws_bytes >= ba_workspace_bytes(plan, 0). */
 ba_status_t branch_attn_fwd(const ba_plan_t *plan,
                             const void *q, const void *k, const void *v,
                             const void *qb, const void *kb, const void *vb,

@@ -15,11 +15,11 @@ namespace {
 // Opt-in per-kernel timing: HIP events recorded on the launch stream.
 enum KernelId {
   K_UPLOAD = 0, K_MAIN_FWD, K_BRANCH_LOCAL_FWD, K_LSE_MERGE, K_BWD_PREPROCESS, K_MAIN_BWD_DQ, K_MAIN_BWD_DKDV,
-  K_BRANCH_LOCAL_BWD, K_DQ_CONVERT, K_VT_TRANSPOSE, K_RING_FWD, K_COUNT
+  K_BRANCH_LOCAL_BWD, K_DQ_CONVERT, K_VT_TRANSPOSE, K_RING_FWD, K_VBT_TRANSPOSE, K_COUNT
 };
 const char *kKernelNames[K_COUNT] = {"metadata_upload", "main_fwd", "branch_local_fwd", "lse_merge",
                                      "bwd_preprocess", "main_bwd_dq", "main_bwd_dkdv", "branch_local_bwd",
-                                     "dq_convert",      "vt_transpose", "ring_step_fwd"};
+                                     "dq_convert",      "vt_transpose", "ring_step_fwd",    "vbt_transpose"};
 
 struct TimingState {
   std::mutex mu;
@@ -103,6 +103,10 @@ Meta make_meta(const ba_plan *pl, const void *ws) {
   m.bwd_order = reinterpret_cast<const int32_t *>(b + L.bwd_order);
   m.vt_tiles = reinterpret_cast<const int32_t *>(b + L.vt_tiles);
   m.vt_base = reinterpret_cast<const int32_t *>(b + L.vt_base);
+  m.brow_lo = reinterpret_cast<const int32_t *>(b + L.brow_lo);
+  m.brow_hi = reinterpret_cast<const int32_t *>(b + L.brow_hi);
+  m.fwd_pair_bk = reinterpret_cast<const int32_t *>(b + L.fwd_pair_bk);
+  m.fwd_triple_bk = reinterpret_cast<const int32_t *>(b + L.fwd_triple_bk);
   m.N = pl->N;
   m.Nq = pl->Nq;
   m.Rb = pl->Rb;
@@ -117,6 +121,7 @@ Meta make_meta(const ba_plan *pl, const void *ws) {
   m.n_fwd_pairs = pl->n_fwd_pairs;
   m.n_fwd_triples = pl->n_fwd_triples;
   m.n_vt_tiles = pl->n_vt_tiles;
+  m.n_vbt_tiles = pl->n_vbt_tiles;
   m.max_branch = pl->max_branch;
   m.scale = pl->scale;
   return m;
@@ -224,14 +229,23 @@ ba_status_t fwd_body(const ba_plan *pl, const void *q, const void *k, const void
   BA_TRY(upload(pl, workspace, st));
   const Meta mt = make_meta(pl, workspace);
   uint8_t *ws = static_cast<uint8_t *>(workspace);
+  if (pl->dtype == BA_BF16) {
+    // The branch keys are the last key tiles of the main kernel's online
+    // softmax: one pass gives every row's final output (no partials, no merge).
+    bf16 *vt = reinterpret_cast<bf16 *>(ws + pl->off_vt);
+    bf16 *vbt = reinterpret_cast<bf16 *>(ws + pl->off_vbt);
+    BA_TRY(timed(K_VT_TRANSPOSE, st, "V transpose",
+                 [&] { return launch_vt_transpose_bf16(mt, (const bf16 *)v, vt, st); }));
+    BA_TRY(timed(K_VBT_TRANSPOSE, st, "branch V transpose",
+                 [&] { return launch_vbt_transpose_bf16(mt, (const bf16 *)vb, vbt, st); }));
+    return timed(K_MAIN_FWD, st, "forward (main prefix and branch keys)", [&] {
+      return launch_main_fwd_fused_bf16(mt, (const bf16 *)q, (const bf16 *)qb, (const bf16 *)k, vt, (const bf16 *)kb,
+                                        vbt, (bf16 *)o, lse, (bf16 *)ob, lseb, st);
+    });
+  }
   float *o_pre = reinterpret_cast<float *>(ws + pl->off_o_pre);
   float *lse_pre = reinterpret_cast<float *>(ws + pl->off_lse_pre);
   BA_TRY(run_main_fwd(pl, mt, q, qb, k, v, o, lse, o_pre, lse_pre, workspace, st));
-  if (pl->dtype == BA_BF16)  // branch-local attention and the merge in one kernel
-    return timed(K_BRANCH_LOCAL_FWD, st, "branch-local forward + merge", [&] {
-      return launch_branch_fwd_bf16(mt, (const bf16 *)qb, (const bf16 *)kb, (const bf16 *)vb, o_pre, lse_pre, nullptr,
-                                    nullptr, (bf16 *)ob, lseb, st);
-    });
   float *o_loc = reinterpret_cast<float *>(ws + pl->off_o_loc);
   float *lse_loc = reinterpret_cast<float *>(ws + pl->off_lse_loc);
   BA_TRY(timed(K_BRANCH_LOCAL_FWD, st, "branch-local forward",
@@ -297,8 +311,7 @@ ba_status_t ba_branch_local_fwd(const ba_plan_t *pl, const void *qb, const void 
   const Meta mt = make_meta(pl, workspace);
   BA_TRY(timed(K_BRANCH_LOCAL_FWD, st, "branch-local forward", [&] {
     if (pl->dtype == BA_BF16)
-      return launch_branch_fwd_bf16(mt, (const bf16 *)qb, (const bf16 *)kb, (const bf16 *)vb, nullptr, nullptr, o_loc,
-                                    lse_loc, nullptr, nullptr, st);
+      return launch_branch_fwd_bf16(mt, (const bf16 *)qb, (const bf16 *)kb, (const bf16 *)vb, o_loc, lse_loc, st);
     return launch_branch_local_fwd(mt, pl->dtype, qb, kb, vb, o_loc, lse_loc, st);
   }));
   return BA_OK;
@@ -416,9 +429,11 @@ ba_status_t branch_attn_bwd(const ba_plan_t *pl, const void *q, const void *k, c
       return launch_bwd_gather_bf16(mt, (const bf16 *)q, (const bf16 *)qb, (const bf16 *)o, (const bf16 *)ob,
                                     (const bf16 *)d_o, (const bf16 *)d_ob, lse, lseb, delta, qt, dot, lt, dtt, et, st);
     }));
-    BA_TRY(timed(K_MAIN_BWD_DQ, st, "main-sequence backward (dq)", [&] {
+    // dQ of every row, over its main prefix and then its branch keys, in bf16
+    BA_TRY(timed(K_MAIN_BWD_DQ, st, "backward (dq)", [&] {
       return launch_main_bwd_dq_bf16(mt, (const bf16 *)q, (const bf16 *)qb, (const bf16 *)k, (const bf16 *)v,
-                                     (const bf16 *)d_o, (const bf16 *)d_ob, lse, lseb, delta, dq_acc, st);
+                                     (const bf16 *)d_o, (const bf16 *)d_ob, lse, lseb, delta, (const bf16 *)kb,
+                                     (const bf16 *)vb, (bf16 *)dq, (bf16 *)dqb, st);
     }));
     // Split key tiles: every dK/dV workgroup adds into zeroed float32
     // accumulators, converted to bf16 afterwards (a fill kernel, not a memset).
@@ -445,14 +460,11 @@ ba_status_t branch_attn_bwd(const ba_plan_t *pl, const void *q, const void *k, c
                                  (float *)dv, st);
     }));
   }
-  if (pl->dtype == BA_BF16) {  // the branch kernel writes dqb itself
-    BA_TRY(timed(K_BRANCH_LOCAL_BWD, st, "branch-local backward", [&] {
+  if (pl->dtype == BA_BF16)  // dK, dV of the branch keys
+    return timed(K_BRANCH_LOCAL_BWD, st, "branch-local backward (dkb, dvb)", [&] {
       return launch_branch_bwd_bf16(mt, (const bf16 *)qb, (const bf16 *)kb, (const bf16 *)vb, (const bf16 *)d_ob, lseb,
-                                    delta, dq_acc, (bf16 *)dqb, (bf16 *)dkb, (bf16 *)dvb, st);
-    }));
-    return timed(K_DQ_CONVERT, st, "dq convert",
-                 [&] { return launch_convert_rows(dq_acc, pl->Nq * hd, dq, pl->dtype, st); });
-  }
+                                    delta, (bf16 *)dkb, (bf16 *)dvb, st);
+    });
   BA_TRY(timed(K_BRANCH_LOCAL_BWD, st, "branch-local backward", [&] {
     return launch_branch_local_bwd(mt, pl->dtype, qb, kb, vb, d_ob, lseb, delta, dq_acc, dkb, dvb, st);
   }));

@@ -15,12 +15,14 @@
 // v_mfma_f32_16x16x16bf16_1k, whose transposed operands come from rows staged
 // in LDS through the transposing LDS read.
 //
-// The forward merges in the same pass: with the main-prefix partial
-// (O_pre, LSE_pre) it writes the final branch output and LSE by the
-// log-sum-exp reduction (Eq. 2 as named in the evolve.pub review, "Scope &
-// Claims"), so the float32 branch-local partial never reaches HBM. The
-// backward adds the branch-local dQ to the float32 accumulator the main
-// backward filled and writes the branch rows' dQ in the output type.
+// These kernels serve the split path: the forward writes the branch-local
+// partial (O_loc, LSE_loc) that lse_merge joins with the main-prefix partial
+// (Eq. 2 as named in the evolve.pub review, "Scope & Claims"); the merged
+// forward of branch_attn_fwd instead takes the branch keys as the last key
+// tiles of the main kernel. The backward gives the branch keys' dK and dV,
+// summed over the anchor's queries; those queries' dQ, branch part included,
+// comes from the main dq kernel, which takes the branch keys as its last key
+// tiles.
 #include <cmath>
 
 #include "launch.hpp"
@@ -91,16 +93,11 @@ __device__ __forceinline__ void stage_branch_rows(bf16 *dst, const bf16 *__restr
 
 }  // namespace
 
-// Forward. MERGE: read the main-prefix partial (o_pre, lse_pre) and write the
-// final output ob (bf16) and LSE lseb; otherwise write the branch-local partial
-// (o_loc float32, lse_loc).
-template <int HD, int KB, bool MERGE>
+// Forward: the branch-local partial (o_loc float32, lse_loc) of the split path.
+template <int HD, int KB>
 __global__ __launch_bounds__(64) void branch_fwd_bf16_kernel(Meta mt, const bf16 *__restrict__ qb,
                                                              const bf16 *__restrict__ kb, const bf16 *__restrict__ vb,
-                                                             const float *__restrict__ o_pre,
-                                                             const float *__restrict__ lse_pre,
-                                                             float *__restrict__ o_loc, float *__restrict__ lse_loc,
-                                                             bf16 *__restrict__ ob, float *__restrict__ lseb) {
+                                                             float *__restrict__ o_loc, float *__restrict__ lse_loc) {
   constexpr int LD = HD + 8;  // LDS row stride (elements): rows 16 bytes apart in bank order
   constexpr int KS = HD / 32, DT = HD / 16;
   __shared__ __attribute__((aligned(16))) bf16 sV[KB * 16 * LD];
@@ -165,17 +162,6 @@ __global__ __launch_bounds__(64) void branch_fwd_bf16_kernel(Meta mt, const bf16
       pk[b] = pack4(fast_exp2(s[b][0] - lse2), fast_exp2(s[b][1] - lse2), fast_exp2(s[b][2] - lse2),
                     fast_exp2(s[b][3] - lse2));
     const float lse_l = lse2 * kLn2;
-    // Merge weights of the two partials (Eq. 2): the merged LSE and each side's share.
-    float fa = 0.0f, fb = 1.0f, lse_out = lse_l;
-    if constexpr (MERGE) {
-      const float a = qv ? lse_pre[(int64_t)h * mt.Rb + row] : 0.0f;
-      const float M = fmaxf(a, lse_l);
-      const float wa = __expf(a - M), wb = __expf(lse_l - M);
-      const float tot = wa + wb;
-      fa = wa / tot;
-      fb = wb / tot;
-      lse_out = M + __logf(tot);
-    }
     // O^T = V^T P^T per 16-wide d block: lane holds query qi, d = dt*16 + 4*(lane/16) .. +3.
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -183,26 +169,13 @@ __global__ __launch_bounds__(64) void branch_fwd_bf16_kernel(Meta mt, const bf16
 #pragma unroll
       for (int b = 0; b < KB; ++b) o = mfma16k16(tr16<LD>(sV, b * 16, dt * 16, lane), pk[b], o);
       const int64_t off = roff + dt * 16 + 4 * (lane >> 4);
-      if (qv) {
-        if constexpr (MERGE) {
-          const f32x4 x = *reinterpret_cast<const f32x4 *>(o_pre + off);
-          const f32x4 z = fa * x + fb * o;
-          const bf16x4 zb = {(bf16)z[0], (bf16)z[1], (bf16)z[2], (bf16)z[3]};
-          *reinterpret_cast<bf16x4 *>(ob + off) = zb;
-        } else {
-          *reinterpret_cast<f32x4 *>(o_loc + off) = o;
-        }
-      }
+      if (qv) *reinterpret_cast<f32x4 *>(o_loc + off) = o;
     }
-    if (qv && lane < 16) {
-      if constexpr (MERGE) lseb[(int64_t)h * mt.Rb + row] = lse_out;
-      else lse_loc[(int64_t)h * mt.Rb + row] = lse_out;
-    }
+    if (qv && lane < 16) lse_loc[(int64_t)h * mt.Rb + row] = lse_l;
   }
 }
 
-// Backward through the final (merged) LSE: P = exp(S - LSE), dS = P (dP - D).
-// dQ of the branch rows = dq_acc (main-prefix part) + scale dS K, written to dqb;
+// Backward through the final (merged) LSE: P = exp(S - LSE), dS = P (dP - D);
 // dKb = scale dS^T Q and dVb = P^T dO summed over the anchor's queries.
 template <int HD, int KB>
 __global__ __launch_bounds__(64) void branch_bwd_bf16_kernel(Meta mt, const bf16 *__restrict__ qb,
@@ -210,12 +183,10 @@ __global__ __launch_bounds__(64) void branch_bwd_bf16_kernel(Meta mt, const bf16
                                                              const bf16 *__restrict__ dob,
                                                              const float *__restrict__ lseb,
                                                              const float *__restrict__ delta,
-                                                             const float *__restrict__ dq_acc, bf16 *__restrict__ dqb,
                                                              bf16 *__restrict__ dkb, bf16 *__restrict__ dvb) {
   constexpr int LD = HD + 8;
   constexpr int LP = KB * 16 + 4;  // row stride of the P and dS blocks
   constexpr int KS = HD / 32, DT = HD / 16;
-  __shared__ __attribute__((aligned(16))) bf16 sK[KB * 16 * LD];
   __shared__ __attribute__((aligned(16))) bf16 sQ[16 * LD];
   __shared__ __attribute__((aligned(16))) bf16 sdO[16 * LD];
   __shared__ __attribute__((aligned(16))) bf16 sP[16 * LP];
@@ -229,7 +200,6 @@ __global__ __launch_bounds__(64) void branch_bwd_bf16_kernel(Meta mt, const bf16
   const float sl2 = mt.scale * kLog2e;
   const int64_t R = mt.Nq + mt.Rb;
 
-  stage_branch_rows<HD, KB, LD>(sK, kb, b0, L, mt.hkv, g, lane);
   // K and V as A operands of S^T and dP^T (lane: key b*16 + lane%16, d 32*ks + 8*(lane/16) .. +7).
   bf16x8 kf[KB][KS], vf[KB][KS];
 #pragma unroll
@@ -259,7 +229,7 @@ __global__ __launch_bounds__(64) void branch_bwd_bf16_kernel(Meta mt, const bf16
     const int h = mt.group_heads[g * G + hj];
     const int64_t row = b0 + j;
     const int64_t roff = (row * hq + h) * HD;
-    __syncthreads();  // the previous block's LDS reads are done (and sK is staged)
+    __syncthreads();  // the previous block's LDS reads are done
     f32x4 s[KB], dp[KB];
 #pragma unroll
     for (int b = 0; b < KB; ++b) {
@@ -297,21 +267,6 @@ __global__ __launch_bounds__(64) void branch_bwd_bf16_kernel(Meta mt, const bf16
       *reinterpret_cast<i16x4 *>(sP + (lane & 15) * LP + b * 16 + 4 * (lane >> 4)) = pk[b];
       *reinterpret_cast<i16x4 *>(sdS + (lane & 15) * LP + b * 16 + 4 * (lane >> 4)) = dsk[b];
     }
-    // dQ^T = K^T dS^T: lane holds query qi, d = dt*16 + 4*(lane/16) .. +3.
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      f32x4 acc = {};
-#pragma unroll
-      for (int b = 0; b < KB; ++b) acc = mfma16k16(tr16<LD>(sK, b * 16, dt * 16, lane), dsk[b], acc);
-      if (qv) {
-        const int64_t off = (mt.Nq + row) * (int64_t)hq * HD + (int64_t)h * HD + dt * 16 + 4 * (lane >> 4);
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(dq_acc + off);
-        const float sc = mt.scale;
-        const bf16x4 y = {(bf16)(x[0] + sc * acc[0]), (bf16)(x[1] + sc * acc[1]), (bf16)(x[2] + sc * acc[2]),
-                          (bf16)(x[3] + sc * acc[3])};
-        *reinterpret_cast<bf16x4 *>(dqb + roff + dt * 16 + 4 * (lane >> 4)) = y;
-      }
-    }
     __syncthreads();  // this block's Q, dO, P and dS rows are in LDS
     // dV^T += dO^T P and dK^T += Q^T dS, contracted over the block's 16 queries.
 #pragma unroll
@@ -342,21 +297,11 @@ __global__ __launch_bounds__(64) void branch_bwd_bf16_kernel(Meta mt, const bf16
   }
 }
 
-hipError_t launch_branch_fwd_bf16(const Meta &mt, const bf16 *qb, const bf16 *kb, const bf16 *vb,
-                                  const float *o_pre, const float *lse_pre, float *o_loc, float *lse_loc, bf16 *ob,
-                                  float *lseb, hipStream_t st) {
+hipError_t launch_branch_fwd_bf16(const Meta &mt, const bf16 *qb, const bf16 *kb, const bf16 *vb, float *o_loc,
+                                  float *lse_loc, hipStream_t st) {
   if (mt.A == 0 || mt.Rb == 0) return hipSuccess;
   const unsigned grid = (unsigned)(mt.A * mt.hkv);
-  const bool merge = o_pre != nullptr;
-#define BA_LAUNCH(HD, KB)                                                                                      \
-  do {                                                                                                         \
-    if (merge)                                                                                                 \
-      branch_fwd_bf16_kernel<HD, KB, true><<<grid, 64, 0, st>>>(mt, qb, kb, vb, o_pre, lse_pre, nullptr,       \
-                                                                 nullptr, ob, lseb);                           \
-    else                                                                                                       \
-      branch_fwd_bf16_kernel<HD, KB, false><<<grid, 64, 0, st>>>(mt, qb, kb, vb, nullptr, nullptr, o_loc,      \
-                                                                  lse_loc, nullptr, nullptr);                  \
-  } while (0)
+#define BA_LAUNCH(HD, KB) branch_fwd_bf16_kernel<HD, KB><<<grid, 64, 0, st>>>(mt, qb, kb, vb, o_loc, lse_loc)
   if (mt.d == 128) {
     BA_LAUNCH(128, 1);
     if (mt.max_branch > 16) BA_LAUNCH(128, 2);
@@ -369,12 +314,11 @@ hipError_t launch_branch_fwd_bf16(const Meta &mt, const bf16 *qb, const bf16 *kb
 }
 
 hipError_t launch_branch_bwd_bf16(const Meta &mt, const bf16 *qb, const bf16 *kb, const bf16 *vb, const bf16 *dob,
-                                  const float *lseb, const float *delta, const float *dq_acc, bf16 *dqb, bf16 *dkb,
-                                  bf16 *dvb, hipStream_t st) {
+                                  const float *lseb, const float *delta, bf16 *dkb, bf16 *dvb, hipStream_t st) {
   if (mt.A == 0 || mt.Rb == 0) return hipSuccess;
   const unsigned grid = (unsigned)(mt.A * mt.hkv);
 #define BA_LAUNCH(HD, KB) \
-  branch_bwd_bf16_kernel<HD, KB><<<grid, 64, 0, st>>>(mt, qb, kb, vb, dob, lseb, delta, dq_acc, dqb, dkb, dvb)
+  branch_bwd_bf16_kernel<HD, KB><<<grid, 64, 0, st>>>(mt, qb, kb, vb, dob, lseb, delta, dkb, dvb)
   if (mt.d == 128) {
     BA_LAUNCH(128, 1);
     if (mt.max_branch > 16) BA_LAUNCH(128, 2);

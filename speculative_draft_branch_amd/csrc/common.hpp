@@ -36,9 +36,13 @@ struct Meta {
   const int32_t *bwd_order;
   const int32_t *vt_tiles;
   const int32_t *vt_base;
+  const int32_t *brow_lo;
+  const int32_t *brow_hi;
+  const int32_t *fwd_pair_bk;
+  const int32_t *fwd_triple_bk;
   int64_t N, Nq, Rb, A;
   int32_t hq, hkv, G, d, rows_per_tile;
-  int32_t n_qtiles, n_ktiles, n_fwd_pairs, n_vt_tiles, n_fwd_triples;
+  int32_t n_qtiles, n_ktiles, n_fwd_pairs, n_vt_tiles, n_fwd_triples, n_vbt_tiles;
   int32_t max_branch;  // longest branch (rows of one anchor)
   float scale;
 };

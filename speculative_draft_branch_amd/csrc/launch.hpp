@@ -15,16 +15,13 @@ hipError_t launch_branch_local_fwd(const Meta &mt, ba_dtype_t dt, const void *qb
 hipError_t launch_branch_local_bwd(const Meta &mt, ba_dtype_t dt, const void *qb, const void *kb, const void *vb,
                                    const void *dob, const float *lseb, const float *delta, float *dq_acc,
                                    void *dkb, void *dvb, hipStream_t st);
-// bf16 branch-local kernels on 16x16 MFMA. Forward: with o_pre non-NULL it
-// merges with the main-prefix partial and writes ob/lseb, else it writes the
-// float32 partial o_loc/lse_loc. Backward: writes dqb = dq_acc (main part) +
-// the branch-local part, and dkb, dvb.
-hipError_t launch_branch_fwd_bf16(const Meta &mt, const bf16 *qb, const bf16 *kb, const bf16 *vb,
-                                  const float *o_pre, const float *lse_pre, float *o_loc, float *lse_loc, bf16 *ob,
-                                  float *lseb, hipStream_t st);
+// bf16 branch-local kernels on 16x16 MFMA. Forward: the float32 partial
+// o_loc/lse_loc of the split path. Backward: dkb, dvb (the branch rows' dQ
+// comes from the main dq kernel, which takes the branch keys as its last tiles).
+hipError_t launch_branch_fwd_bf16(const Meta &mt, const bf16 *qb, const bf16 *kb, const bf16 *vb, float *o_loc,
+                                  float *lse_loc, hipStream_t st);
 hipError_t launch_branch_bwd_bf16(const Meta &mt, const bf16 *qb, const bf16 *kb, const bf16 *vb, const bf16 *dob,
-                                  const float *lseb, const float *delta, const float *dq_acc, bf16 *dqb, bf16 *dkb,
-                                  bf16 *dvb, hipStream_t st);
+                                  const float *lseb, const float *delta, bf16 *dkb, bf16 *dvb, hipStream_t st);
 hipError_t launch_bwd_preprocess(const Meta &mt, ba_dtype_t dt, const void *o, const void *d_o, const void *ob,
                                  const void *d_ob, float *delta, hipStream_t st);
 hipError_t launch_convert_rows(const float *acc, int64_t n, void *out, ba_dtype_t dt, hipStream_t st);
@@ -41,6 +38,11 @@ hipError_t launch_main_bwd_f32(const Meta &mt, const float *q, const float *qb, 
 // written, from v holding the window's rows (row 0 = position win_lo).
 hipError_t launch_vt_transpose_bf16(const Meta &mt, const bf16 *v, bf16 *vt, hipStream_t st, int win_lo = 0,
                                     int win_hi = 0);
+// Forward with the branch keys as the last key tiles of each unit: final o/ob, lse/lseb.
+hipError_t launch_main_fwd_fused_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *vt,
+                                      const bf16 *kb, const bf16 *vbt, bf16 *o, float *lse, bf16 *ob, float *lseb,
+                                      hipStream_t st);
+hipError_t launch_vbt_transpose_bf16(const Meta &mt, const bf16 *vb, bf16 *vbt, hipStream_t st);
 hipError_t launch_main_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *vt,
                                 bf16 *o, float *lse, float *o_pre, float *lse_pre, hipStream_t st);
 // One ring step: every row against the main keys of its prefix inside
@@ -50,7 +52,8 @@ hipError_t launch_ring_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, c
                                 int win_lo, int win_hi, float *o_run, float *lse_run, hipStream_t st);
 hipError_t launch_main_bwd_dq_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *v,
                                    const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
-                                   const float *delta, float *dq_acc, hipStream_t st);
+                                   const float *delta, const bf16 *kb, const bf16 *vb, bf16 *dq, bf16 *dqb,
+                                   hipStream_t st);
 hipError_t launch_bwd_gather_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *o, const bf16 *ob,
                                   const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
                                   float *delta, bf16 *qt, bf16 *dot, float *lt, float *dtt, int *et, hipStream_t st);

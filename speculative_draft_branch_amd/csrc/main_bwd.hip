@@ -14,9 +14,10 @@
 //  * dq: query-tile major, the forward's work unit (query tile x its key range,
 //    64-key LDS tiles). S^T = K Q^T and dP^T = V dO^T put one query row on each
 //    lane (dP^T starts from -D of that row); dQ^T += K^T dS^T takes K through
-//    the transposing LDS read and dS^T straight from registers. dQ is written
-//    once per row (float32, into the accumulator the branch-local backward adds
-//    to).
+//    the transposing LDS read and dS^T straight from registers. The unit's
+//    branch keys (rows of kb, vb) follow its main keys as the last tiles, each
+//    row masked to its own branch's keys, so every row's whole dQ is summed in
+//    registers and written once, in bf16.
 //  * dkdv: key-tile major: 256 main keys of one kv head (eight waves of 32
 //    keys, sharing every staged query tile) against every query tile whose rows
 //    may see them; each wave keeps its keys' dK, dV in registers across all
@@ -53,9 +54,13 @@ constexpr int kDqRing = 4;
 constexpr int kDqKRing = 4;
 
 // MASK: some key of the tile lies past some row's prefix end (a wave-uniform
-// condition, so the unmasked tiles carry no per-element selects).
-template <int HD, bool MASK>
-__device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const bf16 *sV, int k0, float sl2) {
+// condition, so the unmasked tiles carry no per-element selects). BR: a tile
+// of branch keys (branch row indices k0..); the row sees keys [br->x, br->y]
+// of it, read from LDS where they are used (the kernel has no register to keep
+// them in).
+template <int HD, bool MASK, bool BR = false>
+__device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const bf16 *sV, int k0, float sl2,
+                                        const int2 *br = nullptr) {
   constexpr int KS = DqState<HD>::KS, DT = DqState<HD>::DT;
   const int lane = st.lane;
   // One 32-key block at a time: S^T, dP^T, dS^T, then its two dQ k-steps.
@@ -94,10 +99,19 @@ __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const b
       return join(lds_read_tr(sK + lds_off<HD>(key0, d)), lds_read_tr(sK + lds_off<HD>(key0 + 8, d)));
     };
     bf16x8 db[2];  // dS^T operands of the block's two 16-key k-steps
+    int2 bkr = {0, 0};
+    if constexpr (BR) {
+      const int2 *bp = br;
+      asm volatile("" : "+v"(bp));  // read where used, not held across the tile
+      bkr = *bp;
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float p = fast_exp2(fmaf(s[i], sl2, -st.l2));
-      if constexpr (MASK) {
+      if constexpr (BR) {
+        const int key = k0 + kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+        if (key < bkr.x || key > bkr.y) p = 0.0f;
+      } else if constexpr (MASK) {
         const int key = k0 + kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
         if (key > st.end) p = 0.0f;
       }
@@ -123,6 +137,8 @@ __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const b
 // NG: groups of four waves, one query tile each (the forward's work unit): two
 // at d = 128, three at d = 64, where three waves per SIMD fit in the registers
 // and the vector work of one wave's tile meets the MFMAs of two others.
+// The unit's branch keys [bk_lo, bk_hi) (the forward's ranges) follow its main
+// keys in 64-key tiles of kb, vb; dQ of every row goes to dq / dqb in bf16.
 template <int HD, int NG>
 __global__ __launch_bounds__(256 * NG, 1) void main_bwd_dq_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
                                                                const bf16 *__restrict__ qb,
@@ -133,7 +149,9 @@ __global__ __launch_bounds__(256 * NG, 1) void main_bwd_dq_bf16_kernel(Meta mt, 
                                                                const float *__restrict__ lse,
                                                                const float *__restrict__ lseb,
                                                                const float *__restrict__ delta,
-                                                               float *__restrict__ dq_acc) {
+                                                               const bf16 *__restrict__ kb,
+                                                               const bf16 *__restrict__ vb,
+                                                               bf16 *__restrict__ dq, bf16 *__restrict__ dqb) {
   constexpr int BN = 64;
   constexpr int KS = HD / 16, DT = HD / 32;
   // K and V of one buffer share an array (one address for both reads).
@@ -141,6 +159,8 @@ __global__ __launch_bounds__(256 * NG, 1) void main_bwd_dq_bf16_kernel(Meta mt, 
   __shared__ __attribute__((aligned(16))) bf16 sKV1[2 * BN * HD];
   bf16 *const sK0 = sKV0, *const sV0 = sKV0 + BN * HD;
   bf16 *const sK1 = sKV1, *const sV1 = sKV1 + BN * HD;
+  // per MFMA row of each group: the branch keys [x, y] the row sees (x > y: none)
+  __shared__ int2 sBr[NG * 128];
 
   // Work unit: the forward's pair of adjacent query tiles of one sequence
   // (waves 0-3 the first, 4-7 the second) against the union of their key
@@ -163,6 +183,9 @@ __global__ __launch_bounds__(256 * NG, 1) void main_bwd_dq_bf16_kernel(Meta mt, 
   const int64_t R = mt.Nq + mt.Rb;
   const int kv_lo = tile_a.kv_lo, kv_end = max(tile_a.end_max, end_b);
   const int ntiles = (kv_end - kv_lo + BN) / BN;
+  const int *bkr = NG == 2 ? mt.fwd_pair_bk : mt.fwd_triple_bk;
+  const int bk_lo = uni(bkr[2 * unit]), bk_hi = uni(bkr[2 * unit + 1]);
+  const int bt0 = bk_lo / BN, nbt = bk_hi > bk_lo ? (bk_hi - 1) / BN - bt0 + 1 : 0;
   AsyncTile<HD, BN, 512> kvt;
   kvt.init(hkv * HD, tid);
   const bf16 *kg = k + (int64_t)g * HD, *vg = v + (int64_t)g * HD;
@@ -214,6 +237,11 @@ __global__ __launch_bounds__(256 * NG, 1) void main_bwd_dq_bf16_kernel(Meta mt, 
   for (int i = 0; i < 16; ++i) st.nd[i] = -dd;
   st.wmin = wave_min(row >= 0 ? st.end : INT_MAX);
   const int wmax = wave_max(st.end);
+  int2 br = {INT_MAX, -1};
+  if (row >= mt.Nq) br = int2{mt.brow_lo[row - mt.Nq], mt.brow_hi[row - mt.Nq]};
+  const int wbmin = uni(wave_min(br.x)), wbmax = uni(wave_max(br.y));
+  int2 *const sBrw = sBr + grpi * 128 + (wave & 3) * 32;  // this wave's 32 rows
+  if (lane < 32) sBrw[lane] = br;
   const float sl2 = mt.scale * kLog2e;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) st.acc[dt] = f32x16{};
@@ -244,16 +272,29 @@ __global__ __launch_bounds__(256 * NG, 1) void main_bwd_dq_bf16_kernel(Meta mt, 
       else dq_tile<HD, false>(st, sK1, sV1, k0 + BN, sl2);
     }
   }
+  // Branch tiles after the main loop (a few per unit), one at a time in
+  // buffer 0, masked to each row's own branch keys.
+  const bf16 *kbg = kb + (int64_t)g * HD, *vbg = vb + (int64_t)g * HD;
+  for (int jb = 0; jb < nbt; ++jb) {
+    const int b0 = (bt0 + jb) * BN;
+    dma_barrier<0>();  // every wave is done with buffer 0
+    if (dma_wave) {
+      kvt.load(sK0, kbg, b0, (int)mt.Rb - 1);
+      kvt.load(sV0, vbg, b0, (int)mt.Rb - 1);
+    }
+    dma_barrier<0>();  // the tile is in buffer 0
+    if (b0 <= wbmax && b0 + BN - 1 >= wbmin) dq_tile<HD, true, true>(st, sK0, sV0, b0, sl2, sBrw + (lane & 31));
+  }
   if (row >= 0) {
-    float *dst = dq_acc + ((int64_t)row * mt.hq + h) * HD;
+    bf16 *dst = (is_main ? dq : dqb) + roff;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = dt * 32 + q4 * 8 + (lane >> 5) * 4;
-        const f32x4 val = {mt.scale * st.acc[dt][q4 * 4 + 0], mt.scale * st.acc[dt][q4 * 4 + 1],
-                           mt.scale * st.acc[dt][q4 * 4 + 2], mt.scale * st.acc[dt][q4 * 4 + 3]};
-        *reinterpret_cast<f32x4 *>(dst + d) = val;
+        const bf16x4 val = {(bf16)(mt.scale * st.acc[dt][q4 * 4 + 0]), (bf16)(mt.scale * st.acc[dt][q4 * 4 + 1]),
+                            (bf16)(mt.scale * st.acc[dt][q4 * 4 + 2]), (bf16)(mt.scale * st.acc[dt][q4 * 4 + 3])};
+        *reinterpret_cast<bf16x4 *>(dst + d) = val;
       }
   }
 }
@@ -622,14 +663,15 @@ hipError_t launch_bwd_gather_bf16(const Meta &mt, const bf16 *q, const bf16 *qb,
 
 hipError_t launch_main_bwd_dq_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *v,
                                    const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
-                                   const float *delta, float *dq_acc, hipStream_t st) {
+                                   const float *delta, const bf16 *kb, const bf16 *vb, bf16 *dq, bf16 *dqb,
+                                   hipStream_t st) {
   if (mt.n_fwd_pairs == 0) return hipSuccess;
   if (mt.d == 128)
     main_bwd_dq_bf16_kernel<128, 2><<<(unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv), 512, 0, st>>>(
-        mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, dq_acc);
+        mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, kb, vb, dq, dqb);
   else
     main_bwd_dq_bf16_kernel<64, 3><<<(unsigned)((int64_t)mt.n_fwd_triples * mt.hkv), 768, 0, st>>>(
-        mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, dq_acc);
+        mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, kb, vb, dq, dqb);
   return hipGetLastError();
 }
 

@@ -1,11 +1,14 @@
 // Main-sequence forward on bf16 MFMA (gfx950): every query row -- main rows and
 // draft-branch rows alike -- attends its causal main prefix in its own packed
-// sequence, with an online softmax; main rows get their final output and LSE,
-// branch rows a float32 partial (O_pre, LSE_pre) that is merged later with the
-// branch-local partial by the log-sum-exp reduction (evolve.pub review,
-// "Scope & Claims", section 3.2 and Eq. 2; rcap.io explainer, paragraph on
-// branch attention under context parallelism). Branch K/V never enter these
-// tiles.
+// sequence, with an online softmax. In the merged forward (FUSED) the branch
+// rows then take their own branch's keys as the last key tiles of the same
+// softmax, which is the log-sum-exp merge of the main-prefix and branch-local
+// parts taken inside one pass (evolve.pub review, "Scope & Claims", section 3.2
+// and Eq. 2; rcap.io explainer, paragraph on branch attention under context
+// parallelism; cere-bro wiki, "Mechanism"); branch K/V still never join the
+// main-key tiles, and every row's final output is written once. The split-path
+// instantiation instead leaves branch rows a float32 partial (O_pre, LSE_pre)
+// for lse_merge.
 //
 // Work unit: two query tiles of one sequence that are adjacent in prefix-end
 // order (each up to 128 MFMA rows = base rows x q heads of one kv group, sorted
@@ -53,6 +56,8 @@ struct FwdState {
   bool started;  // the running max has been set (wave-uniform)
   int end, wmin, wmax;
   int klo;  // ring step: first key of the window (keys below it are masked)
+  int blo, bhi;      // branch keys (branch row indices) this row sees: [blo, bhi]; none for main rows
+  int wbmin, wbmax;  // smallest blo and largest bhi of the wave
   int lane;
   uint32_t k_base, k_t;  // K row reads
   uint32_t v_base, v_t;  // V^T row reads
@@ -138,12 +143,20 @@ __device__ __forceinline__ float fwd_form_p(const FwdState<HD> &st, const f32x16
   return rs;
 }
 
-template <int HD, bool RING>
+template <int HD, bool RING, bool BRANCH>
 __device__ __forceinline__ void fwd_softmax(FwdState<HD> &st, f32x16 (&s)[2], int k0, float sl2, bf16x8 (&pb)[4]) {
   constexpr int DT = FwdState<HD>::DT;
   const int lane = st.lane;
-  // some key of this tile lies past some row's prefix end (or, in a ring step, before the window)
-  if (k0 + 63 > st.wmin || (RING && k0 < st.klo)) {
+  if constexpr (BRANCH) {  // a tile of branch keys: each row sees its own branch's keys only
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+        if (key < st.blo || key > st.bhi) s[kb][i] = -INFINITY;
+      }
+  } else if (k0 + 63 > st.wmin || (RING && k0 < st.klo)) {
+    // some key of this tile lies past some row's prefix end (or, in a ring step, before the window)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -185,18 +198,30 @@ __device__ __forceinline__ void load_k_tile(const Tile &kt, bf16 *dst, const bf1
 // [win_lo, win_hi) are attended; k holds exactly those rows (row 0 = position
 // win_lo) and vt their V^T tiles; every row's partial is merged into the
 // running float32 (o_run [Nq+Rb][Hq][d], lse_run [Hq][Nq+Rb]) in the epilogue.
+// FUSED: after its main keys the unit takes the branch keys its branch rows
+// see -- the contiguous range [bk_lo, bk_hi) of branch rows, in 64-key tiles of
+// kb and of vbt (the branch V transposed like vt) -- as further key tiles of the
+// same online softmax, each row masked to its own branch's keys (a TTT query j
+// sees keys 1..j of its branch, a block query the whole block). The softmax
+// then covers the union of the row's keys, which is the merged result of the
+// main-prefix and branch-local parts (the log-sum-exp merge, taken inside the
+// pass), so every row's final output goes straight to o / ob (bf16) and lse /
+// lseb, with no partial in HBM. Otherwise branch rows leave a float32 partial
+// of their main prefix in o_pre / lse_pre.
 // NG: groups of four waves, one query tile each. With NG = 3 (the d = 64
 // forward, whose softmax phase is twice its matrix phase) two groups run their
 // softmax beside the third group's MFMAs, which gives the vector units of a
 // SIMD a third more throughput than one softmax wave gets there.
-template <int HD, bool RING, int NG>
+template <int HD, bool RING, int NG, bool FUSED>
 __global__ __launch_bounds__(256 * NG, 1) void main_fwd_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
                                                             const bf16 *__restrict__ qb,
                                                             const bf16 *__restrict__ k,
                                                             const bf16 *__restrict__ vt, bf16 *__restrict__ o,
                                                             float *__restrict__ lse, float *__restrict__ o_pre,
                                                             float *__restrict__ lse_pre, int win_lo, int win_hi,
-                                                            float *__restrict__ o_run, float *__restrict__ lse_run) {
+                                                            float *__restrict__ o_run, float *__restrict__ lse_run,
+                                                            const bf16 *__restrict__ kb, const bf16 *__restrict__ vbt,
+                                                            bf16 *__restrict__ ob, float *__restrict__ lseb) {
   constexpr int BN = 64;  // keys per K/V tile
   constexpr int KS = HD / 16, DT = HD / 32;
   __shared__ __attribute__((aligned(16))) bf16 sK0[BN * HD];
@@ -233,6 +258,14 @@ __global__ __launch_bounds__(256 * NG, 1) void main_fwd_bf16_kernel(Meta mt, con
   }
   const int k_first = kv_lo + t0 * BN;
   const int ntiles = kv_end >= klo ? (kv_end - k_first + BN) / BN : 0;
+  // Fused: branch tiles bt0 .. bt0 + nbt - 1 (64 branch keys each) follow the main tiles.
+  int bt0 = 0, nbt = 0;
+  if constexpr (FUSED) {
+    const int *bk = NG == 2 ? mt.fwd_pair_bk : mt.fwd_triple_bk;
+    const int bk_lo = uni(bk[2 * unit]), bk_hi = uni(bk[2 * unit + 1]);
+    bt0 = bk_lo / BN;
+    nbt = bk_hi > bk_lo ? (bk_hi - 1) / BN - bt0 + 1 : 0;
+  }
 
   // This lane's query row: MFMA row 32*(wave%4) + lane%32 = base row * G + head
   // of the group's tile.
@@ -266,6 +299,16 @@ __global__ __launch_bounds__(256 * NG, 1) void main_fwd_bf16_kernel(Meta mt, con
   }
   st.wmin = wave_min(row >= 0 ? st.end : INT_MAX);
   st.wmax = wave_max(st.end);
+  if constexpr (FUSED) {
+    st.blo = INT_MAX;
+    st.bhi = -1;
+    if (row >= mt.Nq) {
+      st.blo = mt.brow_lo[row - mt.Nq];
+      st.bhi = mt.brow_hi[row - mt.Nq];
+    }
+    st.wbmin = uni(wave_min(st.blo));
+    st.wbmax = uni(wave_max(st.bhi));
+  }
   st.klo = klo;
   st.m_run = -INFINITY;
   st.l_run = 0.0f;
@@ -325,7 +368,7 @@ __global__ __launch_bounds__(256 * NG, 1) void main_fwd_bf16_kernel(Meta mt, con
         } else {  // softmax of tile jj - 1 (group 1 at h2 = 0) or jj (group 0 at h2 = 1)
           const int js = jj - 1 + h2;
           if (js >= 0 && js < ntiles && k_first + js * BN <= st.wmax)
-            fwd_softmax<HD, RING>(st, s, k_first + js * BN, sl2, pb);
+            fwd_softmax<HD, RING, false>(st, s, k_first + js * BN, sl2, pb);
         }
         // Only the end of the tile needs a barrier (the next requests reuse
         // buffers read in this tile); a second one between the phases, which
@@ -335,6 +378,27 @@ __global__ __launch_bounds__(256 * NG, 1) void main_fwd_bf16_kernel(Meta mt, con
     }
   }
 done:
+  if constexpr (FUSED) {
+    // The branch keys, one 64-key tile at a time after the main loop (a few
+    // tiles per unit): S, the softmax masked to each row's own branch keys,
+    // then P V, all in each wave, with no phase offset between the groups.
+    const bf16 *kbg = kb + (int64_t)g * HD;
+    const bf16 *vbtg = vbt + (int64_t)g * (HD * 64);
+    for (int jb = 0; jb < nbt; ++jb) {
+      const int b0 = (bt0 + jb) * BN;
+      dma_barrier<0>();  // every wave is done with buffer 0
+      if (dma_wave) {
+        kt.load(sK0, kbg, b0, (int)mt.Rb - 1);
+        vtt.load(sV0, vbtg + (int64_t)(bt0 + jb) * vt_stride, 0, HD - 1);
+      }
+      dma_barrier<0>();  // the tile is in buffer 0
+      if (b0 <= st.wbmax && b0 + BN - 1 >= st.wbmin) {
+        fwd_mphase<HD, false, true>(st, sV0, sK0, pb, s);
+        fwd_softmax<HD, false, true>(st, s, b0, sl2, pb);
+        fwd_mphase<HD, true, false>(st, sV0, sK0, pb, s);
+      }
+    }
+  }
 
   const float l_tot = half_sum(st.l_run);
   if constexpr (RING) {
@@ -372,9 +436,9 @@ done:
         const int d = dt * 32 + q4 * 8 + (lane >> 5) * 4;
         const f32x4 val = {st.acc[dt][q4 * 4 + 0] * inv, st.acc[dt][q4 * 4 + 1] * inv,
                            st.acc[dt][q4 * 4 + 2] * inv, st.acc[dt][q4 * 4 + 3] * inv};
-        if (is_main) {
+        if (is_main || FUSED) {
           const bf16x4 b = {(bf16)val[0], (bf16)val[1], (bf16)val[2], (bf16)val[3]};
-          *reinterpret_cast<bf16x4 *>(o + roff + d) = b;
+          *reinterpret_cast<bf16x4 *>((is_main ? o : ob) + roff + d) = b;
         } else {
           *reinterpret_cast<f32x4 *>(o_pre + roff + d) = val;
         }
@@ -382,7 +446,7 @@ done:
     if (lane < 32) {
       const float lv = (st.m_run + __log2f(l_tot)) * kLn2;
       if (is_main) lse[(int64_t)h * mt.Nq + row] = lv;
-      else lse_pre[(int64_t)h * mt.Rb + (row - mt.Nq)] = lv;
+      else (FUSED ? lseb : lse_pre)[(int64_t)h * mt.Rb + (row - mt.Nq)] = lv;
     }
   }
 }
@@ -392,16 +456,18 @@ done:
 // group (stored position 8h + 4c + j holds key 8c + 4h + j).
 // Ring step (win_lo < win_hi): only tiles that meet the window are written, v
 // holds the window's rows (row 0 = position win_lo) and keys outside the window
-// are zero.
+// are zero. rows_hi >= 0: the rows of v are branch keys, tile ti holds rows
+// [64 ti, 64 ti + 64), zero from rows_hi on.
 template <int HD>
 __global__ __launch_bounds__(256) void vt_transpose_bf16_kernel(Meta mt, const bf16 *__restrict__ v,
-                                                                bf16 *__restrict__ vt, int win_lo, int win_hi) {
+                                                                bf16 *__restrict__ vt, int win_lo, int win_hi,
+                                                                int rows_hi) {
   constexpr int NCH = HD / 8;
   constexpr int LD = HD + 2;  // padded LDS row (elements) against bank conflicts on the column reads
   __shared__ __attribute__((aligned(16))) bf16 t[64 * LD];
   const int hkv = mt.hkv, g = blockIdx.x % hkv, ti = blockIdx.x / hkv;
-  const int key_lo = mt.vt_tiles[2 * ti];
-  int lo = key_lo, hi = mt.vt_tiles[2 * ti + 1], base = 0;
+  const int key_lo = rows_hi >= 0 ? 64 * ti : mt.vt_tiles[2 * ti];
+  int lo = key_lo, hi = rows_hi >= 0 ? rows_hi : mt.vt_tiles[2 * ti + 1], base = 0;
   if (win_lo < win_hi) {
     lo = max(lo, win_lo);
     hi = min(hi, win_hi);
@@ -437,14 +503,16 @@ __global__ __launch_bounds__(256) void vt_transpose_bf16_kernel(Meta mt, const b
 // Every variant is instantiated explicitly: with two values of the bool
 // parameter launched from this file, this hipcc emitted the host launch stubs
 // of only one of them (the other launch then referenced an undefined stub).
-#define BA_FWD_INSTANCE(HD, RING, NG)                                                                            \
-  template __global__ void main_fwd_bf16_kernel<HD, RING, NG>(Meta, const bf16 *, const bf16 *, const bf16 *,    \
-                                                              const bf16 *, bf16 *, float *, float *, float *, int, \
-                                                              int, float *, float *)
-BA_FWD_INSTANCE(128, false, 2);
-BA_FWD_INSTANCE(64, false, 3);
-BA_FWD_INSTANCE(128, true, 2);
-BA_FWD_INSTANCE(64, true, 2);
+#define BA_FWD_INSTANCE(HD, RING, NG, FUSED)                                                                     \
+  template __global__ void main_fwd_bf16_kernel<HD, RING, NG, FUSED>(                                           \
+      Meta, const bf16 *, const bf16 *, const bf16 *, const bf16 *, bf16 *, float *, float *, float *, int, int,  \
+      float *, float *, const bf16 *, const bf16 *, bf16 *, float *)
+BA_FWD_INSTANCE(128, false, 2, false);
+BA_FWD_INSTANCE(64, false, 3, false);
+BA_FWD_INSTANCE(128, false, 2, true);
+BA_FWD_INSTANCE(64, false, 3, true);
+BA_FWD_INSTANCE(128, true, 2, false);
+BA_FWD_INSTANCE(64, true, 2, false);
 #undef BA_FWD_INSTANCE
 
 hipError_t launch_vt_transpose_bf16(const Meta &mt, const bf16 *v, bf16 *vt, hipStream_t st, int win_lo,
@@ -452,9 +520,19 @@ hipError_t launch_vt_transpose_bf16(const Meta &mt, const bf16 *v, bf16 *vt, hip
   if (mt.n_vt_tiles == 0) return hipSuccess;
   const unsigned grid = (unsigned)((int64_t)mt.n_vt_tiles * mt.hkv);
   if (mt.d == 128)
-    vt_transpose_bf16_kernel<128><<<grid, 256, 0, st>>>(mt, v, vt, win_lo, win_hi);
+    vt_transpose_bf16_kernel<128><<<grid, 256, 0, st>>>(mt, v, vt, win_lo, win_hi, -1);
   else
-    vt_transpose_bf16_kernel<64><<<grid, 256, 0, st>>>(mt, v, vt, win_lo, win_hi);
+    vt_transpose_bf16_kernel<64><<<grid, 256, 0, st>>>(mt, v, vt, win_lo, win_hi, -1);
+  return hipGetLastError();
+}
+
+hipError_t launch_vbt_transpose_bf16(const Meta &mt, const bf16 *vb, bf16 *vbt, hipStream_t st) {
+  if (mt.n_vbt_tiles == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((int64_t)mt.n_vbt_tiles * mt.hkv);
+  if (mt.d == 128)
+    vt_transpose_bf16_kernel<128><<<grid, 256, 0, st>>>(mt, vb, vbt, 0, 0, (int)mt.Rb);
+  else
+    vt_transpose_bf16_kernel<64><<<grid, 256, 0, st>>>(mt, vb, vbt, 0, 0, (int)mt.Rb);
   return hipGetLastError();
 }
 
@@ -462,11 +540,24 @@ hipError_t launch_main_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, c
                                 bf16 *o, float *lse, float *o_pre, float *lse_pre, hipStream_t st) {
   if (mt.n_fwd_pairs == 0) return hipSuccess;
   if (mt.d == 128)
-    main_fwd_bf16_kernel<128, false, 2><<<(unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv), 512, 0, st>>>(
-        mt, q, qb, k, vt, o, lse, o_pre, lse_pre, 0, 0, nullptr, nullptr);
+    main_fwd_bf16_kernel<128, false, 2, false><<<(unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv), 512, 0, st>>>(
+        mt, q, qb, k, vt, o, lse, o_pre, lse_pre, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
   else
-    main_fwd_bf16_kernel<64, false, 3><<<(unsigned)((int64_t)mt.n_fwd_triples * mt.hkv), 768, 0, st>>>(
-        mt, q, qb, k, vt, o, lse, o_pre, lse_pre, 0, 0, nullptr, nullptr);
+    main_fwd_bf16_kernel<64, false, 3, false><<<(unsigned)((int64_t)mt.n_fwd_triples * mt.hkv), 768, 0, st>>>(
+        mt, q, qb, k, vt, o, lse, o_pre, lse_pre, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_main_fwd_fused_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *vt,
+                                      const bf16 *kb, const bf16 *vbt, bf16 *o, float *lse, bf16 *ob, float *lseb,
+                                      hipStream_t st) {
+  if (mt.n_fwd_pairs == 0) return hipSuccess;
+  if (mt.d == 128)
+    main_fwd_bf16_kernel<128, false, 2, true><<<(unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv), 512, 0, st>>>(
+        mt, q, qb, k, vt, o, lse, nullptr, nullptr, 0, 0, nullptr, nullptr, kb, vbt, ob, lseb);
+  else
+    main_fwd_bf16_kernel<64, false, 3, true><<<(unsigned)((int64_t)mt.n_fwd_triples * mt.hkv), 768, 0, st>>>(
+        mt, q, qb, k, vt, o, lse, nullptr, nullptr, 0, 0, nullptr, nullptr, kb, vbt, ob, lseb);
   return hipGetLastError();
 }
 
@@ -475,11 +566,13 @@ hipError_t launch_ring_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, c
   if (mt.n_fwd_pairs == 0 || win_lo >= win_hi) return hipSuccess;
   const unsigned grid = (unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv);
   if (mt.d == 128)
-    main_fwd_bf16_kernel<128, true, 2><<<grid, 512, 0, st>>>(mt, q, qb, k_win, vt, nullptr, nullptr, nullptr, nullptr,
-                                                          win_lo, win_hi, o_run, lse_run);
+    main_fwd_bf16_kernel<128, true, 2, false><<<grid, 512, 0, st>>>(mt, q, qb, k_win, vt, nullptr, nullptr, nullptr,
+                                                                 nullptr, win_lo, win_hi, o_run, lse_run, nullptr,
+                                                                 nullptr, nullptr, nullptr);
   else
-    main_fwd_bf16_kernel<64, true, 2><<<grid, 512, 0, st>>>(mt, q, qb, k_win, vt, nullptr, nullptr, nullptr, nullptr,
-                                                         win_lo, win_hi, o_run, lse_run);
+    main_fwd_bf16_kernel<64, true, 2, false><<<grid, 512, 0, st>>>(mt, q, qb, k_win, vt, nullptr, nullptr, nullptr,
+                                                                nullptr, win_lo, win_hi, o_run, lse_run, nullptr,
+                                                                nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 

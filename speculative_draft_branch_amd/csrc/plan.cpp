@@ -243,6 +243,42 @@ void build(ba_plan *pl) {
   std::vector<int32_t> fwd_pairs = fwd_units(2, pl->n_fwd_pairs);
   std::vector<int32_t> fwd_triples = fwd_units(3, pl->n_fwd_triples);
 
+  // Branch keys each branch row sees (branch row indices, inclusive): from its
+  // anchor's first branch row to itself (TTT) or to the anchor's last (block).
+  std::vector<int32_t> brow_lo(Rb), brow_hi(Rb);
+  for (int64_t m = 0; m < pl->A; ++m)
+    for (int32_t b = pl->cu_branch[m]; b < pl->cu_branch[m + 1]; ++b) {
+      brow_lo[b] = pl->cu_branch[m];
+      brow_hi[b] = pl->mode[m] == BA_BLOCK ? pl->cu_branch[m + 1] - 1 : b;
+    }
+  // The branch keys a forward unit's rows see, [lo, hi) (lo = hi = 0: none).
+  // Branch rows of consecutive tiles belong to consecutive anchors, so the
+  // range is contiguous and spans little more than the unit's branch rows.
+  auto unit_branch_keys = [&](const std::vector<int32_t> &units, int32_t U) {
+    std::vector<int32_t> out(2 * (units.size() / U), 0);
+    for (size_t i = 0; i < units.size() / U; ++i) {
+      int32_t lo = INT32_MAX, hi = 0;
+      for (int32_t u = 0; u < U; ++u) {
+        const int32_t t = units[U * i + u];
+        if (t < 0) continue;
+        for (int32_t r = 0; r < qt[t].nrows; ++r) {
+          const int32_t row = trow_id[(size_t)qt[t].row_begin + r];
+          if (row < Nq) continue;
+          lo = std::min(lo, brow_lo[row - Nq]);
+          hi = std::max(hi, brow_hi[row - Nq] + 1);
+        }
+      }
+      if (hi > 0) {
+        out[2 * i] = lo;
+        out[2 * i + 1] = hi;
+      }
+    }
+    return out;
+  };
+  std::vector<int32_t> fwd_pair_bk = unit_branch_keys(fwd_pairs, 2);
+  std::vector<int32_t> fwd_triple_bk = unit_branch_keys(fwd_triples, 3);
+  pl->n_vbt_tiles = (int32_t)((Rb + 63) / 64);
+
   // Backward key tiles: per sequence, bwd_keys() main keys each; the query
   // tiles that see a key tile are the sequence's tiles whose largest end
   // reaches it.
@@ -342,6 +378,10 @@ void build(ba_plan *pl) {
   L.bwd_order = put(blob, cur, bwd_order);
   L.vt_tiles = put(blob, cur, vt_tiles);
   L.vt_base = put(blob, cur, vt_base);
+  L.brow_lo = put(blob, cur, brow_lo);
+  L.brow_hi = put(blob, cur, brow_hi);
+  L.fwd_pair_bk = put(blob, cur, fwd_pair_bk);
+  L.fwd_triple_bk = put(blob, cur, fwd_triple_bk);
   L.total = cur;
   blob.resize(std::max<size_t>(cur, 256));
 
@@ -352,19 +392,26 @@ void build(ba_plan *pl) {
   const size_t vt_bytes =
       pl->dtype == BA_BF16 ? align_up((size_t)pl->n_vt_tiles * pl->hkv * pl->d * 64 * sizeof(uint16_t), 256) : 0;
   pl->ws_split = base + vt_bytes;
+  // bf16 forward: the branch V^T tiles follow the main ones (the split-path
+  // entry points do not use them)
+  pl->off_vbt = pl->ws_split;
+  const size_t vbt_bytes =
+      pl->dtype == BA_BF16 ? align_up((size_t)pl->n_vbt_tiles * pl->hkv * pl->d * 64 * sizeof(uint16_t), 256) : 0;
   size_t o_bytes = align_up((size_t)Rb * pl->hq * pl->d * f32, 256);
   size_t l_bytes = align_up((size_t)Rb * pl->hq * f32, 256);
   pl->off_o_pre = pl->ws_split;
   pl->off_lse_pre = pl->off_o_pre + o_bytes;
   pl->off_o_loc = pl->off_lse_pre + l_bytes;
   pl->off_lse_loc = pl->off_o_loc + o_bytes;
-  // bf16: the branch-local kernel merges in registers, so the forward needs no
-  // branch-local partial.
-  pl->ws_fwd = pl->dtype == BA_BF16 ? pl->off_o_loc : pl->off_lse_loc + l_bytes;
+  // bf16: the main kernel takes the branch keys as its last key tiles and
+  // writes every row's final output, so the forward needs no partials.
+  pl->ws_fwd = pl->dtype == BA_BF16 ? pl->off_vbt + vbt_bytes : pl->off_lse_loc + l_bytes;
   pl->off_delta = base;
   size_t d_bytes = align_up((size_t)R * pl->hq * f32, 256);
   pl->off_dq_acc = pl->off_delta + d_bytes;
-  size_t cur_b = pl->off_dq_acc + align_up((size_t)R * pl->hq * pl->d * f32, 256);
+  // float32 dQ accumulator: float32 plans only (the bf16 dq kernel sums a row's
+  // whole dQ in registers and writes it once)
+  size_t cur_b = pl->off_dq_acc + (pl->dtype == BA_F32 ? align_up((size_t)R * pl->hq * pl->d * f32, 256) : 0);
   const size_t tiles_g = (size_t)pl->n_qtiles * pl->hkv;
   if (pl->dtype == BA_BF16) {
     const size_t row_bytes = align_up(tiles_g * kTileRows * pl->d * 2, 256);

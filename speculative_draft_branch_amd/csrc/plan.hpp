@@ -63,6 +63,10 @@ struct BlobLayout {
   size_t bwd_order;     // int32 [n_ktiles]: longest-first launch order
   size_t vt_tiles;      // int32 [n_vt_tiles][2]: main keys [lo, hi) of each transposed V tile (lo + 64 > hi allowed)
   size_t vt_base;       // int32 [S]: first transposed V tile of each sequence
+  size_t brow_lo;       // int32 [Rb]: first branch key (branch row index) a branch row sees
+  size_t brow_hi;       // int32 [Rb]: last branch key it sees (inclusive)
+  size_t fwd_pair_bk;   // int32 [n_fwd_pairs][2]: branch keys [lo, hi) the rows of a forward pair see
+  size_t fwd_triple_bk; // int32 [n_fwd_triples][2]: the same for the threes
   size_t total;
 };
 
@@ -80,12 +84,14 @@ struct ba_plan {
   int32_t rows_per_tile;  // base rows per query tile
   int32_t max_branch;     // longest branch (rows of one anchor)
   int32_t n_qtiles, n_ktiles, n_fwd_pairs, n_vt_tiles, n_fwd_triples;
+  int32_t n_vbt_tiles;  // 64-key transposed tiles of the branch V (bf16 forward)
   int64_t pairs[3];
   ba::BlobLayout layout;
   std::vector<uint8_t> blob;  // host copy of the device metadata
   size_t ws_split, ws_fwd, ws_bwd;
   // workspace regions (byte offsets)
   size_t off_vt;                                          // forward, bf16: V^T tiles [n_vt_tiles][Hkv][d][64]
+  size_t off_vbt;                                         // forward, bf16: branch V^T tiles [n_vbt_tiles][Hkv][d][64]
   size_t off_o_pre, off_lse_pre, off_o_loc, off_lse_loc;  // forward
   size_t off_delta, off_dq_acc;                           // backward
   // backward, query-tile order per kv head: Q and dO rows [n_qtiles][Hkv][128][d],

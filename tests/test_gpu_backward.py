@@ -50,6 +50,14 @@ EDGE = {
     "nobranch_bf16_d128": lambda: custom("n", "bf16", 8, 8, 128, [129, 1, 64, 200], None, [], [], [], seed=4),
     "branches_only_bf16": lambda: custom("b", "bf16", 4, 1, 128, [90], [], [0, 17, 89], [5, 16, 32],
                                          [TTT, BLOCK, TTT], seed=4),
+    # no GQA with 32-row branches on every third token: branch keys of a unit span
+    # several 64-key tiles (the dq kernel's branch tiles)
+    "g1_long_branches_bf16_d128": lambda: custom("g1", "bf16", 4, 4, 128, [301, 197], None, list(range(1, 498, 3)),
+                                                 [32 - (i % 3) for i in range(166)],
+                                                 [TTT if i % 2 else BLOCK for i in range(166)], std=1.0, seed=4),
+    "g1_long_branches_bf16_d64": lambda: custom("g1", "bf16", 4, 4, 64, [301, 197], None, list(range(1, 498, 3)),
+                                                [32 - (i % 3) for i in range(166)],
+                                                [TTT if i % 2 else BLOCK for i in range(166)], std=1.0, seed=4),
     # branches longer than 16 rows in both modes at GQA 8:1, d=64 (two 16-key blocks per branch)
     "long_branches_bf16_d64": lambda: custom("l", "bf16", 16, 2, 64, [120, 60], None, [0, 40, 119, 130, 179],
                                              [17, 32, 20, 24, 9], [BLOCK, BLOCK, TTT, TTT, BLOCK], std=1.0, seed=4),

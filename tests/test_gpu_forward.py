@@ -73,6 +73,15 @@ EDGE = {
     # branches longer than 16 rows in both modes at GQA 8:1, d=64 (two 16-key blocks per branch)
     "long_branches_bf16_d64": lambda: _edge("l", "bf16", 64, 16, 2, [120, 60], None, [0, 40, 119, 130, 179],
                                             [17, 32, 20, 24, 9], [BLOCK, BLOCK, TTT, TTT, BLOCK]),
+    # no GQA (128 base rows per tile) with 32-row branches of both modes on every
+    # third token: a unit's branch keys span three or four 64-key tiles and
+    # start off a tile boundary
+    "g1_long_branches_bf16_d128": lambda: _edge("g1", "bf16", 128, 4, 4, [301, 197], None, list(range(1, 498, 3)),
+                                                [32 - (i % 3) for i in range(166)],
+                                                [TTT if i % 2 else BLOCK for i in range(166)]),
+    "g1_long_branches_bf16_d64": lambda: _edge("g1", "bf16", 64, 4, 4, [301, 197], None, list(range(1, 498, 3)),
+                                               [32 - (i % 3) for i in range(166)],
+                                               [TTT if i % 2 else BLOCK for i in range(166)]),
     "peaked_bf16_d64": lambda: _edge("p", "bf16", 64, 16, 2, [700], None, list(range(0, 700, 16)),
                                      [16] * len(range(0, 700, 16)), [BLOCK] * len(range(0, 700, 16)), std=0.5,
                                      qk_scale=4.0),

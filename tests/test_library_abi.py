@@ -20,7 +20,7 @@ INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
 
 
 def _declared_functions():
-    text = open(os.path.join(INCLUDE, "branch_attn.h")).read()
+    text = "".join(open(os.path.join(INCLUDE, f)).read() for f in sorted(os.listdir(INCLUDE)) if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\(", text)
     skip = {"if", "sizeof", "defined", "extern", "typedef"}
@@ -35,7 +35,8 @@ def test_library_exports_every_declared_function():
     assert "branch_attn_fwd_noalloc" in declared
     for name in declared:
         assert hasattr(lib, name), name
-    assert set(declared) == set(sda.exported_symbols())
+    from speculative_draft_branch_amd import tapchannel
+    assert set(declared) == set(sda.exported_symbols()) | set(tapchannel.SYMBOLS)
     assert sda.abi_version() == 1
 
 
@@ -109,8 +110,14 @@ def test_workspace_sizes_cover_partials():
     p = Plan.from_workload(w)
     f32 = 4
     partial = w.Rb * w.num_q_heads * (w.head_dim + 1) * f32  # one float32 (O, LSE) partial of the branch rows
-    # bf16 merges the branch-local part in registers: only the main-prefix partial is stored
-    assert partial <= p.workspace_bytes(0) < 2 * partial
+    # bf16 takes the branch keys inside the main kernel: no partial at all, only
+    # the metadata and the transposed main and branch V tiles
+    vt = (-(-w.N // 64) + -(-w.Rb // 64)) * 64 * w.num_kv_heads * w.head_dim * 2
+    assert vt <= p.workspace_bytes(0) < vt + partial // 8
+    pf = Plan.from_workload(W.get("tiny_f32"))
+    wf = W.get("tiny_f32")
+    # float32: both partials of the split path
+    assert pf.workspace_bytes(0) >= 2 * wf.Rb * wf.num_q_heads * (wf.head_dim + 1) * f32
     assert p.workspace_bytes(1) >= (w.Nq + w.Rb) * w.num_q_heads * (w.head_dim + 1) * f32
     assert 0 < p.workspace_bytes(2) <= p.workspace_bytes(0)
 
