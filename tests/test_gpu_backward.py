@@ -110,7 +110,7 @@ def _identity_checks(w, t, got):
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("name", ["ctx256k_rank3", "gptoss_128k_mixed"])
+@pytest.mark.parametrize("name", ["ctx256k_rank3", "gptoss_128k_mixed", "qwen3_8b_16k", "dflash_64k"])
 def test_backward_full_size(name):
     w = W.get(name)
     say(f"[bwd full] {w.name}: N={w.N} Nq={w.Nq} Rb={w.Rb}")
