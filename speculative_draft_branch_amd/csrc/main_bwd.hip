@@ -393,6 +393,8 @@ namespace {
 // about 164, so twelve waves (three per SIMD, 384 keys) fit, and each wave's
 // elementwise work has two other waves' MFMAs beside it.
 constexpr int kDkdvBlocks = 1;
+// Operands in flight in the dV/dK product stretch (a ring of single operands).
+constexpr int kDkdvRing = 4;
 constexpr int dkdv_threads(int hd) { return 64 * (hd == 64 ? kBwdKeys64 : kBwdKeys) / (32 * kDkdvBlocks); }
 
 template <int HD, int KB>
@@ -497,20 +499,22 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
         const int kk = 2 * rb + n / DT, dt = n % DT;
         return join(pad_tr_read<HD>(sQ, st.t_base, 0, kk, dt), pad_tr_read<HD>(sQ, st.t_base, 1, kk, dt));
       };
-      bf16x8 bo[2], bq[2];
-      bo[0] = rdo(0);
-      bq[0] = rdq(0);
+      // All dV steps, then all dK steps, through one ring of kDkdvRing
+      // operands: a read is issued kDkdvRing - 1 MFMAs before its use.
+      constexpr int NS = 2 * DT;  // steps of each product
+      auto rd = [&](int i) { return i < NS ? rdo(i) : rdq(i - NS); };
+      bf16x8 ring[kDkdvRing];
+#pragma unroll
+      for (int i = 0; i < kDkdvRing - 1; ++i) ring[i] = rd(i);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int n = 0; n < 2 * DT; ++n) {
-        if (n + 1 < 2 * DT) {
-          bo[(n + 1) & 1] = rdo(n + 1);
-          bq[(n + 1) & 1] = rdq(n + 1);
-        }
+      for (int i = 0; i < 2 * NS; ++i) {
+        if (i + kDkdvRing - 1 < 2 * NS) ring[(i + kDkdvRing - 1) % kDkdvRing] = rd(i + kDkdvRing - 1);
+        const int n = i % NS;
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
-          st.adv[b][n % DT] = mfma32(pa[b][n / DT], bo[n & 1], st.adv[b][n % DT]);
-          st.adk[b][n % DT] = mfma32(dsa[b][n / DT], bq[n & 1], st.adk[b][n % DT]);
+          if (i < NS) st.adv[b][n % DT] = mfma32(pa[b][n / DT], ring[i % kDkdvRing], st.adv[b][n % DT]);
+          else st.adk[b][n % DT] = mfma32(dsa[b][n / DT], ring[i % kDkdvRing], st.adk[b][n % DT]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
