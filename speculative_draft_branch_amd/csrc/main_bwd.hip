@@ -423,6 +423,16 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
     // Rows 32rb..32rb+31. element i: row rb*32 + (i/4)*8 + 4*(lane/32) + i%4,
     // key my_key[b].
     bf16x8 pa[KB][2], dsa[KB][2];
+    // Operands of dV += P^T dO and dK += dS^T Q (transposing reads of dO, Q):
+    // step i < NS is dV step i, step NS + n is dK step n; n = (kh, dt).
+    // Operand slot 8*half + 4c + j <-> row 32rb + 16kh + 8c + 4*half + j.
+    constexpr int NS = 2 * DT;
+    auto rd = [&](int i) {
+      const int n = i % NS, kk = 2 * rb + n / DT, dt = n % DT;
+      const bf16 *t = i < NS ? sdO : sQ;
+      return join(pad_tr_read<HD>(t, st.t_base, 0, kk, dt), pad_tr_read<HD>(t, st.t_base, 1, kk, dt));
+    };
+    bf16x8 ring[kDkdvRing];
     {
       // S and dP of these rows, then P and dS element by element from the fp32
       // values (P rounded to bf16 once, for the dV product). The dP accumulator
@@ -467,6 +477,10 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_setprio(0);
+      // The first product operands do not depend on the elementwise step:
+      // their reads are issued before it, so its vector work covers them.
+#pragma unroll
+      for (int i = 0; i < kDkdvRing - 1; ++i) ring[i] = rd(i);
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int r0 = rb * 32 + i4 * 8 + 4 * (lane >> 5);
@@ -485,27 +499,11 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
         }
       }
     }
-    // dV += P^T dO, dK += dS^T Q over these 32 rows (two 16-row k-steps).
-    // Operand slot 8*half + 4c + j <-> row 32rb + 16kh + 8c + 4*half + j.
+    // dV += P^T dO, dK += dS^T Q over these 32 rows (two 16-row k-steps): all
+    // dV steps, then all dK steps, through one ring of kDkdvRing operands, a
+    // read issued kDkdvRing - 1 MFMAs before its use.
     __builtin_amdgcn_s_setprio(1);
     {
-      // Steps n = (kh, dt); the operands of step n + 1 are read while step n
-      // multiplies.
-      auto rdo = [&](int n) {
-        const int kk = 2 * rb + n / DT, dt = n % DT;
-        return join(pad_tr_read<HD>(sdO, st.t_base, 0, kk, dt), pad_tr_read<HD>(sdO, st.t_base, 1, kk, dt));
-      };
-      auto rdq = [&](int n) {
-        const int kk = 2 * rb + n / DT, dt = n % DT;
-        return join(pad_tr_read<HD>(sQ, st.t_base, 0, kk, dt), pad_tr_read<HD>(sQ, st.t_base, 1, kk, dt));
-      };
-      // All dV steps, then all dK steps, through one ring of kDkdvRing
-      // operands: a read is issued kDkdvRing - 1 MFMAs before its use.
-      constexpr int NS = 2 * DT;  // steps of each product
-      auto rd = [&](int i) { return i < NS ? rdo(i) : rdq(i - NS); };
-      bf16x8 ring[kDkdvRing];
-#pragma unroll
-      for (int i = 0; i < kDkdvRing - 1; ++i) ring[i] = rd(i);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 2 * NS; ++i) {
