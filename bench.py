@@ -319,13 +319,10 @@ def hbm_kernels(w, kern):
     """HBM-bound kernels (bf16): algorithmic bytes per launch and the rate
     against the 8 TB/s peak. Branch-local backward (dK, dV of the branch keys),
     per (branch row, q head): Q, dO 4d, LSE and D 8; per (branch row, kv head):
-    K, V in and dK, dV out 8d. Backward gather, per (row, q head): Q, O, dO read
-    and the scaled Q and dO written, 10d, plus LSE, D in and the staged pair and
-    D out, 16."""
+    K, V in and dK, dV out 8d. (The backward preprocess -- D and the staged
+    query tiles -- runs inside the dq kernel.)"""
     rb, hq, hkv, d = w.Rb, w.num_q_heads, w.num_kv_heads, w.head_dim
-    rows = w.Nq + w.Rb
-    byt = {"branch_local_bwd": rb * hq * (4 * d + 8) + rb * hkv * 8 * d,
-           "bwd_preprocess": rows * hq * (10 * d + 16)}
+    byt = {"branch_local_bwd": rb * hq * (4 * d + 8) + rb * hkv * 8 * d}
     out = {}
     for k, b in byt.items():
         if k in kern and kern[k][1]:

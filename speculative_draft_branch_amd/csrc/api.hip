@@ -425,15 +425,15 @@ ba_status_t branch_attn_bwd(const ba_plan_t *pl, const void *q, const void *k, c
     float *lt = reinterpret_cast<float *>(ws + pl->off_lt);
     float *dtt = reinterpret_cast<float *>(ws + pl->off_dt);
     int *et = reinterpret_cast<int *>(ws + pl->off_et);
-    BA_TRY(timed(K_BWD_PREPROCESS, st, "backward preprocess", [&] {
-      return launch_bwd_gather_bf16(mt, (const bf16 *)q, (const bf16 *)qb, (const bf16 *)o, (const bf16 *)ob,
-                                    (const bf16 *)d_o, (const bf16 *)d_ob, lse, lseb, delta, qt, dot, lt, dtt, et, st);
-    }));
-    // dQ of every row, over its main prefix and then its branch keys, in bf16
+    // dQ of every row, over its main prefix and then its branch keys, in bf16;
+    // the same kernel takes D = rowsum(dO * O) and stages the query tiles the
+    // dK/dV kernel streams (the backward preprocess).
+    const BwdStage sg{qt, dot, lt, dtt, et, delta};
     BA_TRY(timed(K_MAIN_BWD_DQ, st, "backward (dq)", [&] {
       return launch_main_bwd_dq_bf16(mt, (const bf16 *)q, (const bf16 *)qb, (const bf16 *)k, (const bf16 *)v,
-                                     (const bf16 *)d_o, (const bf16 *)d_ob, lse, lseb, delta, (const bf16 *)kb,
-                                     (const bf16 *)vb, (bf16 *)dq, (bf16 *)dqb, st);
+                                     (const bf16 *)d_o, (const bf16 *)d_ob, lse, lseb, (const bf16 *)o,
+                                     (const bf16 *)ob, (const bf16 *)kb, (const bf16 *)vb, (bf16 *)dq, (bf16 *)dqb,
+                                     sg, st);
     }));
     // Split key tiles: every dK/dV workgroup adds into zeroed float32
     // accumulators, converted to bf16 afterwards (a fill kernel, not a memset).

@@ -50,13 +50,18 @@ hipError_t launch_main_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, c
 // the running float32 o_run [Nq+Rb][Hq][d] / lse_run [Hq][Nq+Rb].
 hipError_t launch_ring_fwd_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k_win, const bf16 *vt,
                                 int win_lo, int win_hi, float *o_run, float *lse_run, hipStream_t st);
+// What the dq kernel stages for the dK/dV kernel (query-tile order) and the
+// branch-local backward, besides dq and dqb.
+struct BwdStage {
+  bf16 *qt, *dot;   // [n_qtiles][Hkv][128][d]: Q * scale * log2(e) (bf16), dO
+  float *lt, *dtt;  // [n_qtiles][Hkv][128]: -LSE * log2(e), -D
+  int *et;          // [n_qtiles][kTileMetaWords]: row ends, then end_min, end_max, rows
+  float *delta;     // [Hq][Nq + Rb]: D = rowsum(dO * O)
+};
 hipError_t launch_main_bwd_dq_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *v,
                                    const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
-                                   const float *delta, const bf16 *kb, const bf16 *vb, bf16 *dq, bf16 *dqb,
-                                   hipStream_t st);
-hipError_t launch_bwd_gather_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *o, const bf16 *ob,
-                                  const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
-                                  float *delta, bf16 *qt, bf16 *dot, float *lt, float *dtt, int *et, hipStream_t st);
+                                   const bf16 *o, const bf16 *ob, const bf16 *kb, const bf16 *vb, bf16 *dq,
+                                   bf16 *dqb, const BwdStage &sg, hipStream_t st);
 // dkv_acc: null, or float32 dK, dV accumulators [N][Hkv][d] (zeroed) into
 // which every workgroup adds instead of writing dk, dv (plans with split key tiles).
 hipError_t launch_main_bwd_dkdv_bf16(const Meta &mt, const bf16 *k, const bf16 *v, const bf16 *qt, const bf16 *dot,

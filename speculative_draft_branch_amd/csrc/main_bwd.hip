@@ -13,15 +13,16 @@
 // most two terms, so the result does not depend on their order.
 //  * dq: query-tile major, the forward's work unit (query tile x its key range,
 //    64-key LDS tiles). S^T = K Q^T and dP^T = V dO^T put one query row on each
-//    lane (dP^T starts from -D of that row); dQ^T += K^T dS^T takes K through
-//    the transposing LDS read and dS^T straight from registers. The unit's
+//    lane (dP^T starts from -D of that row, which the kernel takes from the
+//    row's dO and O itself); dQ^T += K^T dS^T takes K through the transposing
+//    LDS read and dS^T straight from registers. The unit's
 //    branch keys (rows of kb, vb) follow its main keys as the last tiles, each
 //    row masked to its own branch's keys, so every row's whole dQ is summed in
 //    registers and written once, in bf16.
 //  * dkdv: key-tile major: 256 main keys of one kv head (eight waves of 32
 //    keys, sharing every staged query tile) against every query tile whose rows
 //    may see them; each wave keeps its keys' dK, dV in registers across all
-//    query tiles, written once, summed over the group's q heads. The gather
+//    query tiles, written once, summed over the group's q heads. The dq kernel
 //    stages Q scaled by scale * log2(e) and -LSE * log2(e), -D per row, so the
 //    S and dP MFMAs (started from those) deliver the exponent of P and dP - D.
 //    S = Q K^T puts the key on the lane, so P and dS are directly the A
@@ -148,10 +149,12 @@ __global__ __launch_bounds__(256 * NG, 1) void main_bwd_dq_bf16_kernel(Meta mt, 
                                                                const bf16 *__restrict__ d_ob,
                                                                const float *__restrict__ lse,
                                                                const float *__restrict__ lseb,
-                                                               const float *__restrict__ delta,
+                                                               const bf16 *__restrict__ o,
+                                                               const bf16 *__restrict__ ob,
                                                                const bf16 *__restrict__ kb,
                                                                const bf16 *__restrict__ vb,
-                                                               bf16 *__restrict__ dq, bf16 *__restrict__ dqb) {
+                                                               bf16 *__restrict__ dq, bf16 *__restrict__ dqb,
+                                                               BwdStage sg) {
   constexpr int BN = 64;
   constexpr int KS = HD / 16, DT = HD / 32;
   // K and V of one buffer share an array (one address for both reads).
@@ -161,6 +164,9 @@ __global__ __launch_bounds__(256 * NG, 1) void main_bwd_dq_bf16_kernel(Meta mt, 
   bf16 *const sK1 = sKV1, *const sV1 = sKV1 + BN * HD;
   // per MFMA row of each group: the branch keys [x, y] the row sees (x > y: none)
   __shared__ int2 sBr[NG * 128];
+  // per MFMA row of each group: (row * Hq + h) of a main row, -2 - ((row - Nq) *
+  // Hq + h) of a branch row, -1 for padding (the row copies below)
+  __shared__ int64_t sRowIdx[NG * 128];
 
   // Work unit: the forward's pair of adjacent query tiles of one sequence
   // (waves 0-3 the first, 4-7 the second) against the union of their key
@@ -201,8 +207,9 @@ __global__ __launch_bounds__(256 * NG, 1) void main_bwd_dq_bf16_kernel(Meta mt, 
   st.end = -1;
   const int grpi = wave >> 2;
   const int my_tile = grpi == 0 ? tl[0] : grpi == 1 ? tl[1] : tl[NG - 1];
+  QTile tile{};
   if (my_tile >= 0) {
-    const QTile tile = load_qtile(mt.qtiles + my_tile);
+    tile = load_qtile(mt.qtiles + my_tile);
     if (bi < tile.nrows) {
       row = mt.tile_row_id[tile.row_begin + bi];
       st.end = mt.tile_row_end[tile.row_begin + bi];
@@ -213,36 +220,111 @@ __global__ __launch_bounds__(256 * NG, 1) void main_bwd_dq_bf16_kernel(Meta mt, 
   const int64_t roff = row < 0 ? 0
                        : is_main ? ((int64_t)row * mt.hq + h) * HD
                                  : ((int64_t)(row - mt.Nq) * mt.hq + h) * HD;
+  if (lane < 32)
+    sRowIdx[grpi * 128 + mrow] = row < 0     ? -1
+                                 : is_main ? (int64_t)row * mt.hq + h
+                                           : -2 - ((int64_t)(row - mt.Nq) * mt.hq + h);
+  __syncthreads();  // the table is complete (every wave of the workgroup)
+  // The row's LSE and branch keys, loaded without a branch (a row that has
+  // none reads a word of the staging area instead, and the value is dropped).
+  const float *lp = row < 0 ? sg.lt : is_main ? lse + (int64_t)h * mt.Nq + row : lseb + (int64_t)h * mt.Rb + (row - mt.Nq);
+  const bool has_br = row >= mt.Nq;
+  const int *blp = has_br ? mt.brow_lo + (row - mt.Nq) : sg.et;
+  const int *bhp = has_br ? mt.brow_hi + (row - mt.Nq) : sg.et;
+  const float lrow = *lp;
+  const int br_lo = *blp, br_hi = *bhp;
+  const int2 br = has_br ? int2{br_lo, br_hi} : int2{INT_MAX, -1};
+  // The Q and dO rows of the group's tile for the dK/dV kernel (stored further
+  // down), read by the group's 256 threads as a stream of their own (LPR lanes
+  // per row, whole 16-byte chunks; each row's source from the table above),
+  // not stored from the registers that hold Q and dO: such a store makes the
+  // compiler allocate the main loop's registers differently and serialise its
+  // exponentials (measured 2.4% slower). A padding row reads a chunk of the
+  // staging area instead (dropped).
+  constexpr int LPR = HD / 8, RPP = 256 / LPR, NP = kTileRows / RPP;
+  uint4 cq[NP], cdo[NP];
+  {
+    const int gt = tid & 255, ch = gt % LPR;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int64_t ri = sRowIdx[grpi * 128 + p * RPP + gt / LPR];
+      const bool pad = ri == -1, mn = ri >= 0;
+      const int64_t off = (mn ? ri : -2 - ri) * HD;
+      const bf16 *xs = pad ? sg.qt : (mn ? q : qb) + off;
+      const bf16 *ys = pad ? sg.dot : (mn ? d_o : d_ob) + off;
+      uint4 x = reinterpret_cast<const uint4 *>(xs)[ch];
+      uint4 y = reinterpret_cast<const uint4 *>(ys)[ch];
+      if (pad) x = y = uint4{0u, 0u, 0u, 0u};
+      cq[p] = x;
+      cdo[p] = y;
+    }
+  }
+  // Q, dO and O of the lane's half row (one batch of loads; O only for D).
+  bf16x8 orow[KS];
   {
     const bf16 *qp = (is_main ? q : qb) + roff + 8 * (lane >> 5);
     const bf16 *op = (is_main ? d_o : d_ob) + roff + 8 * (lane >> 5);
+    const bf16 *fp = (is_main ? o : ob) + roff + 8 * (lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (row >= 0) {
         st.qf[ks] = *reinterpret_cast<const bf16x8 *>(qp + 16 * ks);
         st.of[ks] = *reinterpret_cast<const bf16x8 *>(op + 16 * ks);
+        orow[ks] = *reinterpret_cast<const bf16x8 *>(fp + 16 * ks);
       } else {
         st.qf[ks] = bf16x8{};
         st.of[ks] = bf16x8{};
+        orow[ks] = bf16x8{};
       }
     }
   }
-  st.l2 = INFINITY;  // padding rows: P = 0
+  st.l2 = row >= 0 ? lrow * kLog2e : INFINITY;  // padding rows: P = 0
+  // D = rowsum(dO * O): lanes l and l + 32 hold the two halves of a row.
   float dd = 0.0f;
-  if (row >= 0) {
-    st.l2 = (is_main ? lse[(int64_t)h * mt.Nq + row] : lseb[(int64_t)h * mt.Rb + (row - mt.Nq)]) * kLog2e;
-    dd = delta[(int64_t)h * R + row];
-  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dd = fmaf((float)st.of[ks][e], (float)orow[ks][e], dd);
+  dd += __shfl_xor(dd, 32, 64);
 #pragma unroll
   for (int i = 0; i < 16; ++i) st.nd[i] = -dd;
+  const float sl2 = mt.scale * kLog2e;
+  // What the dK/dV kernel streams, in its query-tile order: the tile's 128
+  // MFMA rows with Q scaled by scale * log2(e) (rounded to bf16), dO,
+  // -LSE * log2(e) and -D (the start values of its S and dP accumulators) and
+  // (kv head 0) the row ends and the tile's end range; also D in [Hq, rows]
+  // for the branch-local backward. Padding rows: zero rows, P = 0.
+  if (my_tile >= 0) {
+    const int64_t trow = ((int64_t)my_tile * hkv + g) * kTileRows + mrow;
+    {
+      const int gt = tid & 255, ch = gt % LPR;
+      const int64_t tbase = ((int64_t)my_tile * hkv + g) * kTileRows;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int m = p * RPP + gt / LPR;
+        const bf16x8 xb = __builtin_bit_cast(bf16x8, cq[p]);
+        bf16x8 sq;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sq[e] = (bf16)((float)xb[e] * sl2);
+        reinterpret_cast<uint4 *>(sg.qt + (tbase + m) * HD)[ch] = __builtin_bit_cast(uint4, sq);
+        reinterpret_cast<uint4 *>(sg.dot + (tbase + m) * HD)[ch] = cdo[p];
+      }
+    }
+    if (lane < 32) {
+      sg.lt[trow] = -st.l2;
+      sg.dtt[trow] = row >= 0 ? -dd : 0.0f;
+      if (row >= 0) sg.delta[(int64_t)h * R + row] = dd;
+      if (g == 0) sg.et[(int64_t)my_tile * kTileMetaWords + mrow] = st.end;
+    }
+    if (g == 0 && (wave & 3) == 0 && lane < kTileMetaWords - kTileRows)
+      sg.et[(int64_t)my_tile * kTileMetaWords + kTileRows + lane] =
+          lane == 0 ? tile.end_min : lane == 1 ? tile.end_max : lane == 2 ? tile.nrows * G : 0;
+  }
   st.wmin = wave_min(row >= 0 ? st.end : INT_MAX);
   const int wmax = wave_max(st.end);
-  int2 br = {INT_MAX, -1};
-  if (row >= mt.Nq) br = int2{mt.brow_lo[row - mt.Nq], mt.brow_hi[row - mt.Nq]};
   const int wbmin = uni(wave_min(br.x)), wbmax = uni(wave_max(br.y));
   int2 *const sBrw = sBr + grpi * 128 + (wave & 3) * 32;  // this wave's 32 rows
   if (lane < 32) sBrw[lane] = br;
-  const float sl2 = mt.scale * kLog2e;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) st.acc[dt] = f32x16{};
   st.lane = lane;
@@ -296,92 +378,6 @@ __global__ __launch_bounds__(256 * NG, 1) void main_bwd_dq_bf16_kernel(Meta mt, 
                             (bf16)(mt.scale * st.acc[dt][q4 * 4 + 2]), (bf16)(mt.scale * st.acc[dt][q4 * 4 + 3])};
         *reinterpret_cast<bf16x4 *>(dst + d) = val;
       }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Backward preprocess for the bf16 path, one workgroup per (query tile, kv
-// head): the tile's 128 MFMA rows in order -- Q rows multiplied by
-// scale * log2(e) (rounded to bf16), dO rows, -LSE * log2(e) and -D with
-// D = rowsum(dO * O) (the start values of the dK/dV kernel's S and dP
-// accumulators, so its MFMAs deliver the exponent of P and dP - D directly)
-// -- plus (kv head 0) each row's prefix end, so the
-// key-tile-major kernel streams contiguous 32 KB blocks. Also writes D in the
-// [Hq, rows] layout for the dq and branch-local kernels. Every (row, q head)
-// lies in exactly one (query tile, kv head).
-template <int HD>
-__global__ __launch_bounds__(256) void bwd_gather_bf16_kernel(Meta mt, const bf16 *__restrict__ q,
-                                                              const bf16 *__restrict__ qb,
-                                                              const bf16 *__restrict__ o,
-                                                              const bf16 *__restrict__ ob,
-                                                              const bf16 *__restrict__ d_o,
-                                                              const bf16 *__restrict__ d_ob,
-                                                              const float *__restrict__ lse,
-                                                              const float *__restrict__ lseb,
-                                                              float *__restrict__ delta, bf16 *__restrict__ qt,
-                                                              bf16 *__restrict__ dot, float *__restrict__ lt,
-                                                              float *__restrict__ dtt, int *__restrict__ et) {
-  // Coalesced: LPR lanes take the LPR 16-byte chunks of one row (a row of one
-  // head is contiguous), so each load instruction reads whole rows.
-  constexpr int LPR = HD / 8;          // lanes (16-byte chunks) per row
-  constexpr int RPP = 256 / LPR;       // rows per pass
-  const int hkv = mt.hkv, G = mt.G;
-  const int g = blockIdx.x % hkv;
-  const int qi = blockIdx.x / hkv;
-  const QTile tile = load_qtile(mt.qtiles + qi);
-  const int ch = threadIdx.x % LPR, rsub = threadIdx.x / LPR;
-  const float sl2 = mt.scale * kLog2e;
-#pragma unroll 2
-  for (int pass = 0; pass < kTileRows / RPP; ++pass) {
-    const int m = pass * RPP + rsub;
-    const int bi = m / G, hj = m - bi * G;
-    const int64_t trow = ((int64_t)qi * hkv + g) * kTileRows + m;
-    uint4 *qd = reinterpret_cast<uint4 *>(qt + trow * HD);
-    uint4 *od = reinterpret_cast<uint4 *>(dot + trow * HD);
-    const bool ok = bi < tile.nrows;
-    float dsum = 0.0f;
-    int row = 0, h = 0;
-    bool is_main = false;
-    if (ok) {
-      row = mt.tile_row_id[tile.row_begin + bi];
-      h = mt.group_heads[g * G + hj];
-      is_main = row < mt.Nq;
-      const int64_t off = is_main ? ((int64_t)row * mt.hq + h) * HD : ((int64_t)(row - mt.Nq) * mt.hq + h) * HD;
-      const uint4 x = reinterpret_cast<const uint4 *>((is_main ? q : qb) + off)[ch];
-      const uint4 y = reinterpret_cast<const uint4 *>((is_main ? d_o : d_ob) + off)[ch];
-      const uint4 z = reinterpret_cast<const uint4 *>((is_main ? o : ob) + off)[ch];
-      const bf16x8 xb = __builtin_bit_cast(bf16x8, x);
-      bf16x8 sq;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sq[e] = (bf16)((float)xb[e] * sl2);
-      qd[ch] = __builtin_bit_cast(uint4, sq);
-      od[ch] = y;
-      const bf16x8 yb = __builtin_bit_cast(bf16x8, y), zb = __builtin_bit_cast(bf16x8, z);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dsum = fmaf((float)yb[e], (float)zb[e], dsum);
-    } else {
-      qd[ch] = uint4{0u, 0u, 0u, 0u};
-      od[ch] = uint4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int sh = LPR / 2; sh >= 1; sh >>= 1) dsum += __shfl_xor(dsum, sh, 64);
-    if (ch == 0) {
-      if (ok) {
-        const float l = is_main ? lse[(int64_t)h * mt.Nq + row] : lseb[(int64_t)h * mt.Rb + (row - mt.Nq)];
-        lt[trow] = -l * kLog2e;
-        dtt[trow] = -dsum;
-        delta[(int64_t)h * (mt.Nq + mt.Rb) + row] = dsum;
-      } else {
-        lt[trow] = -INFINITY;  // padding rows: P = 0
-        dtt[trow] = 0.0f;
-      }
-      if (g == 0) et[(int64_t)qi * kTileMetaWords + m] = ok ? mt.tile_row_end[tile.row_begin + bi] : -1;
-    }
-  }
-  if (g == 0 && threadIdx.x < kTileMetaWords - kTileRows) {
-    const int w = threadIdx.x;
-    et[(int64_t)qi * kTileMetaWords + kTileRows + w] =
-        w == 0 ? tile.end_min : w == 1 ? tile.end_max : w == 2 ? tile.nrows * G : 0;
   }
 }
 
@@ -649,31 +645,17 @@ __global__ __launch_bounds__(dkdv_threads(HD), 1) void main_bwd_dkdv_bf16_kernel
     }
 }
 
-hipError_t launch_bwd_gather_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *o, const bf16 *ob,
-                                  const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
-                                  float *delta, bf16 *qt, bf16 *dot, float *lt, float *dtt, int *et, hipStream_t st) {
-  if (mt.n_qtiles == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((int64_t)mt.n_qtiles * mt.hkv);
-  if (mt.d == 128)
-    bwd_gather_bf16_kernel<128><<<grid, 256, 0, st>>>(mt, q, qb, o, ob, d_o, d_ob, lse, lseb, delta, qt, dot, lt,
-                                                      dtt, et);
-  else
-    bwd_gather_bf16_kernel<64><<<grid, 256, 0, st>>>(mt, q, qb, o, ob, d_o, d_ob, lse, lseb, delta, qt, dot, lt,
-                                                     dtt, et);
-  return hipGetLastError();
-}
-
 hipError_t launch_main_bwd_dq_bf16(const Meta &mt, const bf16 *q, const bf16 *qb, const bf16 *k, const bf16 *v,
                                    const bf16 *d_o, const bf16 *d_ob, const float *lse, const float *lseb,
-                                   const float *delta, const bf16 *kb, const bf16 *vb, bf16 *dq, bf16 *dqb,
-                                   hipStream_t st) {
+                                   const bf16 *o, const bf16 *ob, const bf16 *kb, const bf16 *vb, bf16 *dq,
+                                   bf16 *dqb, const BwdStage &sg, hipStream_t st) {
   if (mt.n_fwd_pairs == 0) return hipSuccess;
   if (mt.d == 128)
     main_bwd_dq_bf16_kernel<128, 2><<<(unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv), 512, 0, st>>>(
-        mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, kb, vb, dq, dqb);
+        mt, q, qb, k, v, d_o, d_ob, lse, lseb, o, ob, kb, vb, dq, dqb, sg);
   else
     main_bwd_dq_bf16_kernel<64, 3><<<(unsigned)((int64_t)mt.n_fwd_triples * mt.hkv), 768, 0, st>>>(
-        mt, q, qb, k, v, d_o, d_ob, lse, lseb, delta, kb, vb, dq, dqb);
+        mt, q, qb, k, v, d_o, d_ob, lse, lseb, o, ob, kb, vb, dq, dqb, sg);
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ constexpr int kTileRows = 128;
 constexpr int kBwdKeys = 256;
 constexpr int kBwdKeys64 = 384;
 inline int bwd_keys(int dtype, int d) { return dtype == BA_BF16 && d == 64 ? kBwdKeys64 : kBwdKeys; }
-// Per-query-tile block of row ends the backward gather writes: 128 prefix ends,
+// Per-query-tile block of row ends the dq kernel stages: 128 prefix ends,
 // then the tile's smallest end, largest end and valid MFMA rows (padded to 3 x 64
 // words for whole-wave LDS copies).
 constexpr int kTileMetaWords = 192;
