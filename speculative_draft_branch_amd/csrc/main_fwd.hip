@@ -70,9 +70,12 @@ struct FwdState {
 // stores them in, so lane (d, half) reads 8 consecutive elements of row d.
 //
 // The phase is one software pipeline of (LDS read, MFMA) steps: the operands
-// of the next kRing steps are always in flight, so LDS latency is paid about
-// once per phase rather than once per k-step.
-constexpr int kRing = 6;
+// of the next ring steps are always in flight, so LDS latency is paid about
+// once per phase rather than once per k-step. Six at d = 128; three at d = 64,
+// where three waves per SIMD leave 168 registers a wave: with six the kernel
+// spilled, and reloaded the spilled DMA addresses inside the tile loop (4.8%
+// slower).
+constexpr int fwd_ring(int hd) { return hd == 64 ? 3 : 6; }
 
 template <int HD, bool PV, bool S>
 __device__ __forceinline__ void fwd_mphase(FwdState<HD> &st, const bf16 *sVt, const bf16 *sK, const bf16x8 (&pb)[4],
@@ -81,7 +84,7 @@ __device__ __forceinline__ void fwd_mphase(FwdState<HD> &st, const bf16 *sVt, co
   constexpr int NPV = PV ? 4 * DT : 0;  // step i < NPV: kk = i / DT, dt = i % DT
   constexpr int NS = S ? 2 * KS : 0;    // then step NPV + j: ks = j / 2, kb = j % 2
   constexpr int N = NPV + NS;
-  constexpr int R = kRing < N ? kRing : N;
+  constexpr int R = fwd_ring(HD) < N ? fwd_ring(HD) : N;
   auto rd = [&](int i) -> bf16x8 {
     if (i < NPV) return row_read<64>(sVt, st.v_base, st.v_t, i % DT, i / DT);
     const int j = i - NPV;
