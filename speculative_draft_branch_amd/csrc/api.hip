@@ -107,6 +107,8 @@ Meta make_meta(const ba_plan *pl, const void *ws) {
   m.brow_hi = reinterpret_cast<const int32_t *>(b + L.brow_hi);
   m.fwd_pair_bk = reinterpret_cast<const int32_t *>(b + L.fwd_pair_bk);
   m.fwd_triple_bk = reinterpret_cast<const int32_t *>(b + L.fwd_triple_bk);
+  m.fwd_unit_bt = reinterpret_cast<const int32_t *>(b + L.fwd_unit_bt);
+  m.vbt_start = reinterpret_cast<const int32_t *>(b + L.vbt_start);
   m.N = pl->N;
   m.Nq = pl->Nq;
   m.Rb = pl->Rb;

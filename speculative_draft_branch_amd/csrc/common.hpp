@@ -40,6 +40,8 @@ struct Meta {
   const int32_t *brow_hi;
   const int32_t *fwd_pair_bk;
   const int32_t *fwd_triple_bk;
+  const int32_t *fwd_unit_bt;
+  const int32_t *vbt_start;
   int64_t N, Nq, Rb, A;
   int32_t hq, hkv, G, d, rows_per_tile;
   int32_t n_qtiles, n_ktiles, n_fwd_pairs, n_vt_tiles, n_fwd_triples, n_vbt_tiles;

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256 * NG, 1) void main_bwd_dq_bf16_kernel(Meta mt, 
   const int ntiles = (kv_end - kv_lo + BN) / BN;
   const int *bkr = NG == 2 ? mt.fwd_pair_bk : mt.fwd_triple_bk;
   const int bk_lo = uni(bkr[2 * unit]), bk_hi = uni(bkr[2 * unit + 1]);
-  const int bt0 = bk_lo / BN, nbt = bk_hi > bk_lo ? (bk_hi - 1) / BN - bt0 + 1 : 0;
+  const int nbt = (bk_hi - bk_lo + BN - 1) / BN;  // 64-key tiles from bk_lo on (0 when none)
   AsyncTile<HD, BN, 512> kvt;
   kvt.init(hkv * HD, tid);
   const bf16 *kg = k + (int64_t)g * HD, *vg = v + (int64_t)g * HD;
@@ -354,11 +354,12 @@ __global__ __launch_bounds__(256 * NG, 1) void main_bwd_dq_bf16_kernel(Meta mt, 
       else dq_tile<HD, false>(st, sK1, sV1, k0 + BN, sl2);
     }
   }
-  // Branch tiles after the main loop (a few per unit), one at a time in
-  // buffer 0, masked to each row's own branch keys.
+  // Branch tiles after the main loop (a few per unit, starting at the unit's
+  // first branch key, so a unit whose branch keys fit in 64 takes one), one at
+  // a time in buffer 0, masked to each row's own branch keys.
   const bf16 *kbg = kb + (int64_t)g * HD, *vbg = vb + (int64_t)g * HD;
   for (int jb = 0; jb < nbt; ++jb) {
-    const int b0 = (bt0 + jb) * BN;
+    const int b0 = bk_lo + jb * BN;
     dma_barrier<0>();  // every wave is done with buffer 0
     if (dma_wave) {
       kvt.load(sK0, kbg, b0, (int)mt.Rb - 1);

@@ -202,8 +202,10 @@ __device__ __forceinline__ void load_k_tile(const Tile &kt, bf16 *dst, const bf1
 // win_lo) and vt their V^T tiles; every row's partial is merged into the
 // running float32 (o_run [Nq+Rb][Hq][d], lse_run [Hq][Nq+Rb]) in the epilogue.
 // FUSED: after its main keys the unit takes the branch keys its branch rows
-// see -- the contiguous range [bk_lo, bk_hi) of branch rows, in 64-key tiles of
-// kb and of vbt (the branch V transposed like vt) -- as further key tiles of the
+// see -- the contiguous range [bk_lo, bk_hi) of branch rows, in 64-key tiles
+// from bk_lo on (rows of kb; the unit's own tiles of vbt, the branch V
+// transposed like vt, so a range that fits in 64 keys is one tile wherever
+// it starts) -- as further key tiles of the
 // same online softmax, each row masked to its own branch's keys (a TTT query j
 // sees keys 1..j of its branch, a block query the whole block). The softmax
 // then covers the union of the row's keys, which is the merged result of the
@@ -261,13 +263,15 @@ __global__ __launch_bounds__(256 * NG, 1) void main_fwd_bf16_kernel(Meta mt, con
   }
   const int k_first = kv_lo + t0 * BN;
   const int ntiles = kv_end >= klo ? (kv_end - k_first + BN) / BN : 0;
-  // Fused: branch tiles bt0 .. bt0 + nbt - 1 (64 branch keys each) follow the main tiles.
-  int bt0 = 0, nbt = 0;
+  // Fused: nbt branch tiles follow the main tiles, 64 branch keys each from
+  // the unit's first branch key b_first; their V^T tiles from vbt tile bt0 on.
+  int b_first = 0, bt0 = 0, nbt = 0;
   if constexpr (FUSED) {
     const int *bk = NG == 2 ? mt.fwd_pair_bk : mt.fwd_triple_bk;
     const int bk_lo = uni(bk[2 * unit]), bk_hi = uni(bk[2 * unit + 1]);
-    bt0 = bk_lo / BN;
-    nbt = bk_hi > bk_lo ? (bk_hi - 1) / BN - bt0 + 1 : 0;
+    b_first = bk_lo;
+    bt0 = uni(mt.fwd_unit_bt[unit]);
+    nbt = (bk_hi - bk_lo + BN - 1) / BN;
   }
 
   // This lane's query row: MFMA row 32*(wave%4) + lane%32 = base row * G + head
@@ -388,7 +392,7 @@ done:
     const bf16 *kbg = kb + (int64_t)g * HD;
     const bf16 *vbtg = vbt + (int64_t)g * (HD * 64);
     for (int jb = 0; jb < nbt; ++jb) {
-      const int b0 = (bt0 + jb) * BN;
+      const int b0 = b_first + jb * BN;
       dma_barrier<0>();  // every wave is done with buffer 0
       if (dma_wave) {
         kt.load(sK0, kbg, b0, (int)mt.Rb - 1);
@@ -460,7 +464,7 @@ done:
 // Ring step (win_lo < win_hi): only tiles that meet the window are written, v
 // holds the window's rows (row 0 = position win_lo) and keys outside the window
 // are zero. rows_hi >= 0: the rows of v are branch keys, tile ti holds rows
-// [64 ti, 64 ti + 64), zero from rows_hi on.
+// [vbt_start[ti], vbt_start[ti] + 64), zero from rows_hi on.
 template <int HD>
 __global__ __launch_bounds__(256) void vt_transpose_bf16_kernel(Meta mt, const bf16 *__restrict__ v,
                                                                 bf16 *__restrict__ vt, int win_lo, int win_hi,
@@ -469,7 +473,7 @@ __global__ __launch_bounds__(256) void vt_transpose_bf16_kernel(Meta mt, const b
   constexpr int LD = HD + 2;  // padded LDS row (elements) against bank conflicts on the column reads
   __shared__ __attribute__((aligned(16))) bf16 t[64 * LD];
   const int hkv = mt.hkv, g = blockIdx.x % hkv, ti = blockIdx.x / hkv;
-  const int key_lo = rows_hi >= 0 ? 64 * ti : mt.vt_tiles[2 * ti];
+  const int key_lo = rows_hi >= 0 ? mt.vbt_start[ti] : mt.vt_tiles[2 * ti];
   int lo = key_lo, hi = rows_hi >= 0 ? rows_hi : mt.vt_tiles[2 * ti + 1], base = 0;
   if (win_lo < win_hi) {
     lo = max(lo, win_lo);

@@ -277,7 +277,16 @@ void build(ba_plan *pl) {
   };
   std::vector<int32_t> fwd_pair_bk = unit_branch_keys(fwd_pairs, 2);
   std::vector<int32_t> fwd_triple_bk = unit_branch_keys(fwd_triples, 3);
-  pl->n_vbt_tiles = (int32_t)((Rb + 63) / 64);
+  // Branch V^T tiles of the bf16 forward (pairs at d = 128, threes at d = 64):
+  // each unit's branch keys in 64-key tiles from its first one, so a unit
+  // whose branch keys fit in 64 takes one tile wherever they start.
+  const std::vector<int32_t> &unit_bk = pl->d == 64 ? fwd_triple_bk : fwd_pair_bk;
+  std::vector<int32_t> fwd_unit_bt(unit_bk.size() / 2), vbt_start;
+  for (size_t u = 0; u < fwd_unit_bt.size(); ++u) {
+    fwd_unit_bt[u] = (int32_t)vbt_start.size();
+    for (int32_t b = unit_bk[2 * u]; b < unit_bk[2 * u + 1]; b += 64) vbt_start.push_back(b);
+  }
+  pl->n_vbt_tiles = (int32_t)vbt_start.size();
 
   // Backward key tiles: per sequence, bwd_keys() main keys each; the query
   // tiles that see a key tile are the sequence's tiles whose largest end
@@ -382,6 +391,8 @@ void build(ba_plan *pl) {
   L.brow_hi = put(blob, cur, brow_hi);
   L.fwd_pair_bk = put(blob, cur, fwd_pair_bk);
   L.fwd_triple_bk = put(blob, cur, fwd_triple_bk);
+  L.fwd_unit_bt = put(blob, cur, fwd_unit_bt);
+  L.vbt_start = put(blob, cur, vbt_start);
   L.total = cur;
   blob.resize(std::max<size_t>(cur, 256));
 

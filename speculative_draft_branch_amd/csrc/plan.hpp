@@ -67,6 +67,8 @@ struct BlobLayout {
   size_t brow_hi;       // int32 [Rb]: last branch key it sees (inclusive)
   size_t fwd_pair_bk;   // int32 [n_fwd_pairs][2]: branch keys [lo, hi) the rows of a forward pair see
   size_t fwd_triple_bk; // int32 [n_fwd_triples][2]: the same for the threes
+  size_t fwd_unit_bt;   // int32 [units of the bf16 forward]: first branch V^T tile of each unit
+  size_t vbt_start;     // int32 [n_vbt_tiles]: first branch key of each branch V^T tile
   size_t total;
 };
 
@@ -84,7 +86,7 @@ struct ba_plan {
   int32_t rows_per_tile;  // base rows per query tile
   int32_t max_branch;     // longest branch (rows of one anchor)
   int32_t n_qtiles, n_ktiles, n_fwd_pairs, n_vt_tiles, n_fwd_triples;
-  int32_t n_vbt_tiles;  // 64-key transposed tiles of the branch V (bf16 forward)
+  int32_t n_vbt_tiles;  // 64-key transposed tiles of the branch V (bf16 forward), per unit from its first branch key
   int64_t pairs[3];
   ba::BlobLayout layout;
   std::vector<uint8_t> blob;  // host copy of the device metadata

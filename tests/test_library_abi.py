@@ -111,7 +111,8 @@ def test_workspace_sizes_cover_partials():
     f32 = 4
     partial = w.Rb * w.num_q_heads * (w.head_dim + 1) * f32  # one float32 (O, LSE) partial of the branch rows
     # bf16 takes the branch keys inside the main kernel: no partial at all, only
-    # the metadata and the transposed main and branch V tiles
+    # the metadata and the transposed main and branch V tiles (the branch tiles
+    # per forward unit, which together cover every branch key at least once)
     vt = (-(-w.N // 64) + -(-w.Rb // 64)) * 64 * w.num_kv_heads * w.head_dim * 2
     assert vt <= p.workspace_bytes(0) < vt + partial // 8
     pf = Plan.from_workload(W.get("tiny_f32"))
