@@ -224,16 +224,22 @@ ba_status_t scratch_of_current_device(void **out) {
   return BA_OK;
 }
 
+// 32-bit words of the work-counter region (the whole region, a multiple of 64,
+// which the fill kernel's 4-word steps cover exactly).
+int64_t queue_words(const ba_plan *pl) { return (int64_t)(pl->off_vt - pl->off_queue) / 4; }
+
 // The forward pass after argument checks: workspace of at least
 // ba_workspace_bytes(plan, 0) bytes.
 ba_status_t fwd_body(const ba_plan *pl, const void *q, const void *k, const void *v, const void *qb, const void *kb,
                      const void *vb, void *o, float *lse, void *ob, float *lseb, void *workspace, hipStream_t st) {
   BA_TRY(upload(pl, workspace, st));
-  const Meta mt = make_meta(pl, workspace);
+  Meta mt = make_meta(pl, workspace);
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   if (pl->dtype == BA_BF16) {
     // The branch keys are the last key tiles of the main kernel's online
     // softmax: one pass gives every row's final output (no partials, no merge).
+    // Its workgroups take their units from per-kv-head counters.
+    mt.queue_units = reinterpret_cast<int *>(ws + pl->off_queue);
     bf16 *vt = reinterpret_cast<bf16 *>(ws + pl->off_vt);
     bf16 *vbt = reinterpret_cast<bf16 *>(ws + pl->off_vbt);
     BA_TRY(timed(K_VT_TRANSPOSE, st, "V transpose",
@@ -241,6 +247,8 @@ ba_status_t fwd_body(const ba_plan *pl, const void *q, const void *k, const void
     BA_TRY(timed(K_VBT_TRANSPOSE, st, "branch V transpose",
                  [&] { return launch_vbt_transpose_bf16(mt, (const bf16 *)vb, vbt, st); }));
     return timed(K_MAIN_FWD, st, "forward (main prefix and branch keys)", [&] {
+      hipError_t e = launch_fill_f32(reinterpret_cast<float *>(mt.queue_units), queue_words(pl), 0.0f, st);
+      if (e != hipSuccess) return e;
       return launch_main_fwd_fused_bf16(mt, (const bf16 *)q, (const bf16 *)qb, (const bf16 *)k, vt, (const bf16 *)kb,
                                         vbt, (bf16 *)o, lse, (bf16 *)ob, lseb, st);
     });
@@ -417,7 +425,7 @@ ba_status_t branch_attn_bwd(const ba_plan_t *pl, const void *q, const void *k, c
   BA_TRY(check_ws(pl, workspace, ws_bytes, 1));
   hipStream_t st = static_cast<hipStream_t>(stream);
   BA_TRY(upload(pl, workspace, st));
-  const Meta mt = make_meta(pl, workspace);
+  Meta mt = make_meta(pl, workspace);
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   float *delta = reinterpret_cast<float *>(ws + pl->off_delta);
   float *dq_acc = reinterpret_cast<float *>(ws + pl->off_dq_acc);
@@ -431,7 +439,12 @@ ba_status_t branch_attn_bwd(const ba_plan_t *pl, const void *q, const void *k, c
     // the same kernel takes D = rowsum(dO * O) and stages the query tiles the
     // dK/dV kernel streams (the backward preprocess).
     const BwdStage sg{qt, dot, lt, dtt, et, delta};
+    // Both kernels take their work items from per-kv-head counters.
+    mt.queue_units = reinterpret_cast<int *>(ws + pl->off_queue);
+    mt.queue_ktiles = mt.queue_units + pl->hkv;
     BA_TRY(timed(K_MAIN_BWD_DQ, st, "backward (dq)", [&] {
+      hipError_t e = launch_fill_f32(reinterpret_cast<float *>(mt.queue_units), queue_words(pl), 0.0f, st);
+      if (e != hipSuccess) return e;
       return launch_main_bwd_dq_bf16(mt, (const bf16 *)q, (const bf16 *)qb, (const bf16 *)k, (const bf16 *)v,
                                      (const bf16 *)d_o, (const bf16 *)d_ob, lse, lseb, (const bf16 *)o,
                                      (const bf16 *)ob, (const bf16 *)kb, (const bf16 *)vb, (bf16 *)dq, (bf16 *)dqb,

@@ -42,6 +42,11 @@ struct Meta {
   const int32_t *fwd_triple_bk;
   const int32_t *fwd_unit_bt;
   const int32_t *vbt_start;
+  // Work counters (zeroed before the launch), one per kv head, or null: the
+  // forward / dQ kernel (queue_units) and the dK/dV kernel (queue_ktiles) then
+  // take their items by block index instead.
+  int *queue_units;
+  int *queue_ktiles;
   int64_t N, Nq, Rb, A;
   int32_t hq, hkv, G, d, rows_per_tile;
   int32_t n_qtiles, n_ktiles, n_fwd_pairs, n_vt_tiles, n_fwd_triples, n_vbt_tiles;
@@ -58,6 +63,47 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf
 // Tile descriptors are the same for every lane; reading them through
 // readfirstlane keeps tile-level control and addressing in scalar registers.
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Work assignment across the XCDs. Items are (index, kv head), numbered index *
+// hkv + head, each head's indices in longest-first order; block index b stands
+// for item b, so the hardware's round-robin of workgroups over the eight XCDs
+// gives each XCD one kv head (its K/V stream through that XCD's L2). The XCDs
+// do not run at one speed, though (identical heads finished up to 6% apart), so
+// with a counter per head a workgroup takes the next index of its XCD's own
+// head and, once that head is done, of any other head: the XCDs then finish
+// together. Returns the item, or -1 when every head is done (the workgroup has
+// nothing to do). One thread calls it; `counters` holds hkv ints, zeroed before
+// the launch.
+__device__ __forceinline__ int take_item(int *counters, int n, int hkv) {
+  const int xcc = (int)__builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11));  // XCC_ID[3:0]
+  for (int h = hkv >= 8 ? xcc : xcc % hkv; h < hkv; h += 8) {
+    const int i = atomicAdd(counters + h, 1);
+    if (i < n) return i * hkv + h;
+  }
+  for (int h = 0; h < hkv; ++h) {
+    const int i = atomicAdd(counters + h, 1);
+    if (i < n) return i * hkv + h;
+  }
+  return -1;
+}
+
+// Workgroups to launch for `items` items: with counters an eighth more (at
+// least 8), since each XCD is dealt a fixed share of the workgroups and one
+// that runs ahead needs spare ones to take over items of the others' heads;
+// the spares that find every head done end at once. Without counters, one
+// workgroup per item.
+inline unsigned queue_grid(int64_t items, const int *counters) {
+  return (unsigned)(counters ? items + (items / 8 > 8 ? items / 8 : 8) : items);
+}
+
+// take_item for the whole workgroup (slot: a __shared__ int); counters null:
+// the block index.
+__device__ __forceinline__ int workgroup_item(int *counters, int n, int hkv, int *slot) {
+  if (!counters) return (int)blockIdx.x;
+  if (threadIdx.x == 0) *slot = take_item(counters, n, hkv);
+  __syncthreads();
+  return *slot;
+}
 __device__ __forceinline__ QTile load_qtile(const QTile *p) {
   QTile t = *p;
   t.row_begin = uni(t.row_begin);

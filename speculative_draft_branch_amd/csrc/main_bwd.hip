@@ -174,8 +174,11 @@ __global__ __launch_bounds__(256 * NG, 1) void main_bwd_dq_bf16_kernel(Meta mt, 
   // XCD's L2 has to hold.
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hkv = mt.hkv, G = mt.G;
-  const int g = blockIdx.x % hkv;
-  const int unit = blockIdx.x / hkv;
+  __shared__ int sItem;
+  const int item = workgroup_item(mt.queue_units, NG == 2 ? mt.n_fwd_pairs : mt.n_fwd_triples, hkv, &sItem);
+  if (item < 0) return;  // every unit is taken (the whole workgroup)
+  const int g = item % hkv;
+  const int unit = item / hkv;
   int tl[NG];
 #pragma unroll
   for (int u = 0; u < NG; ++u) tl[u] = uni(NG == 2 ? mt.fwd_pairs[2 * unit + u] : mt.fwd_triples[NG * unit + u]);
@@ -561,8 +564,11 @@ __global__ __launch_bounds__(dkdv_threads(HD), 1) void main_bwd_dkdv_bf16_kernel
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hkv = mt.hkv;
-  const int g = blockIdx.x % hkv;
-  const KTile kt = load_ktile(mt.ktiles + uni(mt.bwd_order[blockIdx.x / hkv]));
+  __shared__ int sItem;
+  const int item = workgroup_item(mt.queue_ktiles, mt.n_ktiles, hkv, &sItem);
+  if (item < 0) return;  // every key tile is taken (the whole workgroup)
+  const int g = item % hkv;
+  const KTile kt = load_ktile(mt.ktiles + uni(mt.bwd_order[item / hkv]));
 
   // Query tile qi, kv head g -> one LDS buffer (all asynchronous). The row
   // metadata goes first: an address the compiler keeps in scratch is reloaded
@@ -652,10 +658,10 @@ hipError_t launch_main_bwd_dq_bf16(const Meta &mt, const bf16 *q, const bf16 *qb
                                    bf16 *dqb, const BwdStage &sg, hipStream_t st) {
   if (mt.n_fwd_pairs == 0) return hipSuccess;
   if (mt.d == 128)
-    main_bwd_dq_bf16_kernel<128, 2><<<(unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv), 512, 0, st>>>(
+    main_bwd_dq_bf16_kernel<128, 2><<<queue_grid((int64_t)mt.n_fwd_pairs * mt.hkv, mt.queue_units), 512, 0, st>>>(
         mt, q, qb, k, v, d_o, d_ob, lse, lseb, o, ob, kb, vb, dq, dqb, sg);
   else
-    main_bwd_dq_bf16_kernel<64, 3><<<(unsigned)((int64_t)mt.n_fwd_triples * mt.hkv), 768, 0, st>>>(
+    main_bwd_dq_bf16_kernel<64, 3><<<queue_grid((int64_t)mt.n_fwd_triples * mt.hkv, mt.queue_units), 768, 0, st>>>(
         mt, q, qb, k, v, d_o, d_ob, lse, lseb, o, ob, kb, vb, dq, dqb, sg);
   return hipGetLastError();
 }
@@ -664,7 +670,7 @@ hipError_t launch_main_bwd_dkdv_bf16(const Meta &mt, const bf16 *k, const bf16 *
                                      const float *lt, const float *dtt, const int *et, bf16 *dk, bf16 *dv,
                                      float *dkv_acc, hipStream_t st) {
   if (mt.n_ktiles == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((int64_t)mt.n_ktiles * mt.hkv);
+  const unsigned grid = queue_grid((int64_t)mt.n_ktiles * mt.hkv, mt.queue_ktiles);
   if (mt.d == 128)
     main_bwd_dkdv_bf16_kernel<128><<<grid, dkdv_threads(128), 0, st>>>(mt, k, v, qt, dot, lt, dtt, et, dk, dv,
                                                                         dkv_acc);

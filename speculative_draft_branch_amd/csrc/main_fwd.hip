@@ -238,8 +238,11 @@ __global__ __launch_bounds__(256 * NG, 1) void main_fwd_bf16_kernel(Meta mt, con
   const int grpi = wave >> 2;  // group: 0 runs one phase ahead of the others
   const int gp = grpi == 0 ? 0 : 1;  // the phase order of the wave's group
   const int hkv = mt.hkv, G = mt.G;
-  const int g = blockIdx.x % hkv;
-  const int unit = blockIdx.x / hkv;
+  __shared__ int sItem;
+  const int item = workgroup_item(mt.queue_units, NG == 2 ? mt.n_fwd_pairs : mt.n_fwd_triples, hkv, &sItem);
+  if (item < 0) return;  // every unit is taken (the whole workgroup)
+  const int g = item % hkv;
+  const int unit = item / hkv;
   int tl[NG];
 #pragma unroll
   for (int u = 0; u < NG; ++u) tl[u] = uni(NG == 2 ? mt.fwd_pairs[2 * unit + u] : mt.fwd_triples[NG * unit + u]);
@@ -560,11 +563,13 @@ hipError_t launch_main_fwd_fused_bf16(const Meta &mt, const bf16 *q, const bf16 
                                       hipStream_t st) {
   if (mt.n_fwd_pairs == 0) return hipSuccess;
   if (mt.d == 128)
-    main_fwd_bf16_kernel<128, false, 2, true><<<(unsigned)((int64_t)mt.n_fwd_pairs * mt.hkv), 512, 0, st>>>(
-        mt, q, qb, k, vt, o, lse, nullptr, nullptr, 0, 0, nullptr, nullptr, kb, vbt, ob, lseb);
+    main_fwd_bf16_kernel<128, false, 2, true>
+        <<<queue_grid((int64_t)mt.n_fwd_pairs * mt.hkv, mt.queue_units), 512, 0, st>>>(
+            mt, q, qb, k, vt, o, lse, nullptr, nullptr, 0, 0, nullptr, nullptr, kb, vbt, ob, lseb);
   else
-    main_fwd_bf16_kernel<64, false, 3, true><<<(unsigned)((int64_t)mt.n_fwd_triples * mt.hkv), 768, 0, st>>>(
-        mt, q, qb, k, vt, o, lse, nullptr, nullptr, 0, 0, nullptr, nullptr, kb, vbt, ob, lseb);
+    main_fwd_bf16_kernel<64, false, 3, true>
+        <<<queue_grid((int64_t)mt.n_fwd_triples * mt.hkv, mt.queue_units), 768, 0, st>>>(
+            mt, q, qb, k, vt, o, lse, nullptr, nullptr, 0, 0, nullptr, nullptr, kb, vbt, ob, lseb);
   return hipGetLastError();
 }
 

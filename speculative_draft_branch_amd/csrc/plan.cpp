@@ -399,6 +399,8 @@ void build(ba_plan *pl) {
   // Workspace layouts.
   const size_t f32 = sizeof(float);
   size_t base = align_up(blob.size(), 256);
+  pl->off_queue = base;
+  base += align_up((size_t)2 * pl->hkv * sizeof(int32_t), 256);
   pl->off_vt = base;
   const size_t vt_bytes =
       pl->dtype == BA_BF16 ? align_up((size_t)pl->n_vt_tiles * pl->hkv * pl->d * 64 * sizeof(uint16_t), 256) : 0;

@@ -92,6 +92,7 @@ struct ba_plan {
   std::vector<uint8_t> blob;  // host copy of the device metadata
   size_t ws_split, ws_fwd, ws_bwd;
   // workspace regions (byte offsets)
+  size_t off_queue;  // int32 [2][Hkv]: work counters of the forward or dQ kernel, then of the dK/dV kernel
   size_t off_vt;                                          // forward, bf16: V^T tiles [n_vt_tiles][Hkv][d][64]
   size_t off_vbt;                                         // forward, bf16: branch V^T tiles [n_vbt_tiles][Hkv][d][64]
   size_t off_o_pre, off_lse_pre, off_o_loc, off_lse_loc;  // forward
