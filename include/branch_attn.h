@@ -37,7 +37,10 @@
  *     workspace, and must keep them alive until the stream has run the work.
  *   - Workspaces must be ordinary (coarse-grained) device memory, as from
  *     hipMalloc or a torch CUDA tensor: the backward of plans with split key
- *     tiles adds into the workspace with float32 atomics that assume it.
+ *     tiles adds into the workspace with float32 atomics that assume it, and
+ *     the bf16 forward and backward kernels take their work items from
+ *     counters in the workspace (reset by the call itself). A workspace holds
+ *     one call's state: calls that may overlap in time need separate ones.
  *   - Errors are status codes; no C++ exception crosses this boundary. A
  *     non-OK status leaves a message for ba_last_error() (thread-local).
  *     NaN/Inf in the data are propagated, never checked.
@@ -135,8 +138,8 @@ ba_status_t branch_attn_fwd(const ba_plan_t *plan,
 
 /* For callers that cannot allocate (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): branch_attn_fwd without a
- * workspace argument. Its scratch (plan metadata, transposed V tiles and the
- * float32 main-prefix partial of the branch rows) lives in a fixed array of
+ * workspace argument. Its scratch (plan metadata, work counters, transposed V
+ * tiles; for float32 plans the float32 partials) lives in a fixed array of
  * ba_fwd_noalloc_max_bytes() = 64 MiB of device memory per GPU, which the
  * library holds from its first use on that GPU until the process ends; the
  * call allocates and frees nothing. Problems whose ba_workspace_bytes(plan, 0)
