@@ -9,6 +9,23 @@
 
 using namespace ba;
 
+namespace ba {
+
+unsigned persistent_grid(int64_t items, const int *counters) {
+  if (!counters) return (unsigned)items;
+  static std::atomic<int> cus[64];  // compute units per device, 0 until read
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cus[dev].load();
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev].store(n);
+  }
+  return (unsigned)std::min<int64_t>(items, n);
+}
+
+}  // namespace ba
+
 namespace {
 
 // ---------------------------------------------------------------------------

@@ -87,14 +87,20 @@ __device__ __forceinline__ int take_item(int *counters, int n, int hkv) {
   return -1;
 }
 
-// Workgroups to launch for `items` items: with counters an eighth more (at
-// least 8), since each XCD is dealt a fixed share of the workgroups and one
-// that runs ahead needs spare ones to take over items of the others' heads;
-// the spares that find every head done end at once. Without counters, one
-// workgroup per item.
+// Workgroups to launch for `items` items of a kernel that takes one item per
+// workgroup: with counters an eighth more (at least 8), since each XCD is dealt
+// a fixed share of the workgroups and one that runs ahead needs spare ones to
+// take over items of the others' heads; the spares that find every head done
+// end at once. Without counters, one workgroup per item.
 inline unsigned queue_grid(int64_t items, const int *counters) {
   return (unsigned)(counters ? items + (items / 8 > 8 ? items / 8 : 8) : items);
 }
+
+// Workgroups to launch for a kernel whose workgroups loop over items while
+// the counters last (the d = 128 forward): one per compute unit of the current
+// device (that kernel fits one workgroup per compute unit), at most one per
+// item; without counters, one per item.
+unsigned persistent_grid(int64_t items, const int *counters);
 
 // take_item for the whole workgroup (slot: a __shared__ int); counters null:
 // the block index.

@@ -239,225 +239,231 @@ __global__ __launch_bounds__(256 * NG, 1) void main_fwd_bf16_kernel(Meta mt, con
   const int gp = grpi == 0 ? 0 : 1;  // the phase order of the wave's group
   const int hkv = mt.hkv, G = mt.G;
   __shared__ int sItem;
-  const int item = workgroup_item(mt.queue_units, NG == 2 ? mt.n_fwd_pairs : mt.n_fwd_triples, hkv, &sItem);
-  if (item < 0) return;  // every unit is taken (the whole workgroup)
-  const int g = item % hkv;
-  const int unit = item / hkv;
-  int tl[NG];
+  // At d = 128 the workgroups loop over items while the counters hand them out
+  // (one workgroup per compute unit); at d = 64 (the loop there costs spills)
+  // and with no counters, one item per workgroup.
+  for (;;) {
+    const int item = workgroup_item(mt.queue_units, NG == 2 ? mt.n_fwd_pairs : mt.n_fwd_triples, hkv, &sItem);
+    if (item < 0) return;  // every unit is taken (the whole workgroup)
+    const int g = item % hkv;
+    const int unit = item / hkv;
+    int tl[NG];
 #pragma unroll
-  for (int u = 0; u < NG; ++u) tl[u] = uni(NG == 2 ? mt.fwd_pairs[2 * unit + u] : mt.fwd_triples[NG * unit + u]);
-  const int ta = tl[0];
-  const QTile tile_a = load_qtile(mt.qtiles + ta);
-  int end_b = -1;
+    for (int u = 0; u < NG; ++u) tl[u] = uni(NG == 2 ? mt.fwd_pairs[2 * unit + u] : mt.fwd_triples[NG * unit + u]);
+    const int ta = tl[0];
+    const QTile tile_a = load_qtile(mt.qtiles + ta);
+    int end_b = -1;
 #pragma unroll
-  for (int u = 1; u < NG; ++u)
-    if (tl[u] >= 0) end_b = max(end_b, uni(mt.qtiles[tl[u]].end_max));
-  // With NG = 3 the DMA of a 64 x 64 tile (eight 1 KB blocks) is issued by waves 0-7.
-  const bool dma_wave = NG == 2 || wave < 8;
-  // Keys [k_first + 64j, ...) for j < ntiles; k_first is the sequence start, or
-  // in a ring step the start of the sequence's 64-key tile holding the window
-  // start (tile t0 of the sequence), and keys before klo are masked.
-  const int kv_lo = tile_a.kv_lo;
-  int kv_end = max(tile_a.end_max, end_b), klo = kv_lo, t0 = 0;
-  if constexpr (RING) {
-    klo = max(kv_lo, win_lo);
-    t0 = (klo - kv_lo) / BN;
-    kv_end = min(kv_end, win_hi - 1);
-  }
-  const int k_first = kv_lo + t0 * BN;
-  const int ntiles = kv_end >= klo ? (kv_end - k_first + BN) / BN : 0;
-  // Fused: nbt branch tiles follow the main tiles, 64 branch keys each from
-  // the unit's first branch key b_first; their V^T tiles from vbt tile bt0 on.
-  int b_first = 0, bt0 = 0, nbt = 0;
-  if constexpr (FUSED) {
-    const int *bk = NG == 2 ? mt.fwd_pair_bk : mt.fwd_triple_bk;
-    const int bk_lo = uni(bk[2 * unit]), bk_hi = uni(bk[2 * unit + 1]);
-    b_first = bk_lo;
-    bt0 = uni(mt.fwd_unit_bt[unit]);
-    nbt = (bk_hi - bk_lo + BN - 1) / BN;
-  }
-
-  // This lane's query row: MFMA row 32*(wave%4) + lane%32 = base row * G + head
-  // of the group's tile.
-  FwdState<HD> st;
-  const int mrow = (wave & 3) * 32 + (lane & 31);
-  const int bi = mrow / G, hj = mrow - bi * G;
-  int row = -1;
-  st.end = -1;
-  const int my_tile = grpi == 0 ? tl[0] : grpi == 1 ? tl[1] : tl[NG - 1];
-  if (my_tile >= 0) {
-    const QTile tile = load_qtile(mt.qtiles + my_tile);
-    if (bi < tile.nrows) {
-      row = mt.tile_row_id[tile.row_begin + bi];
-      st.end = mt.tile_row_end[tile.row_begin + bi];
-      if constexpr (RING) st.end = min(st.end, win_hi - 1);  // may fall below klo: the row sees no key
+    for (int u = 1; u < NG; ++u)
+      if (tl[u] >= 0) end_b = max(end_b, uni(mt.qtiles[tl[u]].end_max));
+    // With NG = 3 the DMA of a 64 x 64 tile (eight 1 KB blocks) is issued by waves 0-7.
+    const bool dma_wave = NG == 2 || wave < 8;
+    // Keys [k_first + 64j, ...) for j < ntiles; k_first is the sequence start, or
+    // in a ring step the start of the sequence's 64-key tile holding the window
+    // start (tile t0 of the sequence), and keys before klo are masked.
+    const int kv_lo = tile_a.kv_lo;
+    int kv_end = max(tile_a.end_max, end_b), klo = kv_lo, t0 = 0;
+    if constexpr (RING) {
+      klo = max(kv_lo, win_lo);
+      t0 = (klo - kv_lo) / BN;
+      kv_end = min(kv_end, win_hi - 1);
     }
-  }
-  const int h = mt.group_heads[g * G + hj];
-  const bool is_main = row >= 0 && row < mt.Nq;
-  const int64_t roff = row < 0 ? 0
-                       : is_main ? ((int64_t)row * mt.hq + h) * HD
-                                 : ((int64_t)(row - mt.Nq) * mt.hq + h) * HD;
-  // Q as the B operand: lane holds row lane%32, d = 16*ks + 8*(lane/32) + 0..7.
-  {
-    const bf16 *qp = (is_main ? q : qb) + roff + 8 * (lane >> 5);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (row >= 0) st.qf[ks] = *reinterpret_cast<const bf16x8 *>(qp + 16 * ks);
-      else st.qf[ks] = bf16x8{};
+    const int k_first = kv_lo + t0 * BN;
+    const int ntiles = kv_end >= klo ? (kv_end - k_first + BN) / BN : 0;
+    // Fused: nbt branch tiles follow the main tiles, 64 branch keys each from
+    // the unit's first branch key b_first; their V^T tiles from vbt tile bt0 on.
+    int b_first = 0, bt0 = 0, nbt = 0;
+    if constexpr (FUSED) {
+      const int *bk = NG == 2 ? mt.fwd_pair_bk : mt.fwd_triple_bk;
+      const int bk_lo = uni(bk[2 * unit]), bk_hi = uni(bk[2 * unit + 1]);
+      b_first = bk_lo;
+      bt0 = uni(mt.fwd_unit_bt[unit]);
+      nbt = (bk_hi - bk_lo + BN - 1) / BN;
     }
-  }
-  st.wmin = wave_min(row >= 0 ? st.end : INT_MAX);
-  st.wmax = wave_max(st.end);
-  if constexpr (FUSED) {
-    st.blo = INT_MAX;
-    st.bhi = -1;
-    if (row >= mt.Nq) {
-      st.blo = mt.brow_lo[row - mt.Nq];
-      st.bhi = mt.brow_hi[row - mt.Nq];
+
+    // This lane's query row: MFMA row 32*(wave%4) + lane%32 = base row * G + head
+    // of the group's tile.
+    FwdState<HD> st;
+    const int mrow = (wave & 3) * 32 + (lane & 31);
+    const int bi = mrow / G, hj = mrow - bi * G;
+    int row = -1;
+    st.end = -1;
+    const int my_tile = grpi == 0 ? tl[0] : grpi == 1 ? tl[1] : tl[NG - 1];
+    if (my_tile >= 0) {
+      const QTile tile = load_qtile(mt.qtiles + my_tile);
+      if (bi < tile.nrows) {
+        row = mt.tile_row_id[tile.row_begin + bi];
+        st.end = mt.tile_row_end[tile.row_begin + bi];
+        if constexpr (RING) st.end = min(st.end, win_hi - 1);  // may fall below klo: the row sees no key
+      }
     }
-    st.wbmin = uni(wave_min(st.blo));
-    st.wbmax = uni(wave_max(st.bhi));
-  }
-  st.klo = klo;
-  st.m_run = -INFINITY;
-  st.l_run = 0.0f;
-  st.started = false;
+    const int h = mt.group_heads[g * G + hj];
+    const bool is_main = row >= 0 && row < mt.Nq;
+    const int64_t roff = row < 0 ? 0
+                         : is_main ? ((int64_t)row * mt.hq + h) * HD
+                                   : ((int64_t)(row - mt.Nq) * mt.hq + h) * HD;
+    // Q as the B operand: lane holds row lane%32, d = 16*ks + 8*(lane/32) + 0..7.
+    {
+      const bf16 *qp = (is_main ? q : qb) + roff + 8 * (lane >> 5);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) st.acc[dt] = f32x16{};
-  st.lane = lane;
-  row_read_init<HD>(lane & 31, lane, st.k_base, st.k_t);
-  row_read_init<64>(lane & 31, lane, st.v_base, st.v_t);
-  const float sl2 = mt.scale * kLog2e;
+      for (int ks = 0; ks < KS; ++ks) {
+        if (row >= 0) st.qf[ks] = *reinterpret_cast<const bf16x8 *>(qp + 16 * ks);
+        else st.qf[ks] = bf16x8{};
+      }
+    }
+    st.wmin = wave_min(row >= 0 ? st.end : INT_MAX);
+    st.wmax = wave_max(st.end);
+    if constexpr (FUSED) {
+      st.blo = INT_MAX;
+      st.bhi = -1;
+      if (row >= mt.Nq) {
+        st.blo = mt.brow_lo[row - mt.Nq];
+        st.bhi = mt.brow_hi[row - mt.Nq];
+      }
+      st.wbmin = uni(wave_min(st.blo));
+      st.wbmax = uni(wave_max(st.bhi));
+    }
+    st.klo = klo;
+    st.m_run = -INFINITY;
+    st.l_run = 0.0f;
+    st.started = false;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st.acc[dt] = f32x16{};
+    st.lane = lane;
+    row_read_init<HD>(lane & 31, lane, st.k_base, st.k_t);
+    row_read_init<64>(lane & 31, lane, st.v_base, st.v_t);
+    const float sl2 = mt.scale * kLog2e;
 
-  // K tiles: 64 keys x d from the [N][Hkv][d] tensor; V^T tiles: d rows x 64
-  // keys, whole tiles of this sequence's transposed copy.
-  AsyncTile<HD, BN, 512> kt;
-  kt.init(hkv * HD, tid);
-  AsyncTile<64, HD, 512> vtt;
-  vtt.init(64, tid);
-  const bf16 *kg = k + (int64_t)g * HD;
-  const bf16 *vtg = vt + ((int64_t)(mt.vt_base[tile_a.seq] + t0) * hkv + g) * (HD * 64);
-  const int64_t vt_stride = (int64_t)hkv * HD * 64;  // between consecutive V^T tiles
-  // K rows are addressed relative to the buffer's first position (the window
-  // start in a ring step); a ring step's first tile may begin before it.
-  const int kb0 = RING ? win_lo : 0;
-  if (ntiles > 0 && dma_wave) load_k_tile<RING>(kt, sK0, kg, k_first, kb0, klo, kv_end);
-  dma_barrier<0>();
+    // K tiles: 64 keys x d from the [N][Hkv][d] tensor; V^T tiles: d rows x 64
+    // keys, whole tiles of this sequence's transposed copy.
+    AsyncTile<HD, BN, 512> kt;
+    kt.init(hkv * HD, tid);
+    AsyncTile<64, HD, 512> vtt;
+    vtt.init(64, tid);
+    const bf16 *kg = k + (int64_t)g * HD;
+    const bf16 *vtg = vt + ((int64_t)(mt.vt_base[tile_a.seq] + t0) * hkv + g) * (HD * 64);
+    const int64_t vt_stride = (int64_t)hkv * HD * 64;  // between consecutive V^T tiles
+    // K rows are addressed relative to the buffer's first position (the window
+    // start in a ring step); a ring step's first tile may begin before it.
+    const int kb0 = RING ? win_lo : 0;
+    if (ntiles > 0 && dma_wave) load_k_tile<RING>(kt, sK0, kg, k_first, kb0, klo, kv_end);
+    dma_barrier<0>();
 
-  // Phase slots: slot t runs, for group grpi, local phase u = t - grpi; even u
-  // is the matrix phase of tile j = u/2 (P V of tile j-1, S of tile j), odd u
-  // the softmax of tile (u-1)/2. Tile j's K is in buffer j%2 from slot 2j, its
-  // V in buffer j%2 from slot 2j+2; both are requested at slot 2j-2 and 2j
-  // respectively, so every DMA has two phases to land. The loop is unrolled
-  // over the tile parity, so every buffer address is a constant.
-  f32x16 s[2];
-  bf16x8 pb[4];
-  const int nslots = 2 * ntiles + 2;
-  for (int j = 0;; j += 2) {
+    // Phase slots: slot t runs, for group grpi, local phase u = t - grpi; even u
+    // is the matrix phase of tile j = u/2 (P V of tile j-1, S of tile j), odd u
+    // the softmax of tile (u-1)/2. Tile j's K is in buffer j%2 from slot 2j, its
+    // V in buffer j%2 from slot 2j+2; both are requested at slot 2j-2 and 2j
+    // respectively, so every DMA has two phases to land. The loop is unrolled
+    // over the tile parity, so every buffer address is a constant.
+    f32x16 s[2];
+    bf16x8 pb[4];
+    const int nslots = 2 * ntiles + 2;
+    for (int j = 0;; j += 2) {
 #pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int jj = j + par;  // tile whose matrix phase falls in these two slots
-      bf16 *const sKc = par ? sK1 : sK0, *const sKn = par ? sK0 : sK1;
-      bf16 *const sVc = par ? sV1 : sV0, *const sVp = par ? sV0 : sV1;
-      // slot 2jj: requests, then group 0 matrix phase of jj, group 1 softmax of jj-1
-      if (2 * jj >= nslots) goto done;
-      if (jj + 1 < ntiles && dma_wave) load_k_tile<RING>(kt, sKn, kg, k_first + (jj + 1) * BN, kb0, klo, kv_end);
-      if (jj < ntiles && dma_wave) vtt.load(sVc, vtg + jj * vt_stride, 0, HD - 1);
+      for (int par = 0; par < 2; ++par) {
+        const int jj = j + par;  // tile whose matrix phase falls in these two slots
+        bf16 *const sKc = par ? sK1 : sK0, *const sKn = par ? sK0 : sK1;
+        bf16 *const sVc = par ? sV1 : sV0, *const sVp = par ? sV0 : sV1;
+        // slot 2jj: requests, then group 0 matrix phase of jj, group 1 softmax of jj-1
+        if (2 * jj >= nslots) goto done;
+        if (jj + 1 < ntiles && dma_wave) load_k_tile<RING>(kt, sKn, kg, k_first + (jj + 1) * BN, kb0, klo, kv_end);
+        if (jj < ntiles && dma_wave) vtt.load(sVc, vtg + jj * vt_stride, 0, HD - 1);
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        if (h2 == 1 && 2 * jj + 1 >= nslots) goto done;
-        if (gp == h2) {  // matrix phase of tile jj
-          const bool do_pv = jj >= 1 && jj <= ntiles && k_first + (jj - 1) * BN <= st.wmax;
-          const bool do_s = jj < ntiles && k_first + jj * BN <= st.wmax;
-          __builtin_amdgcn_s_setprio(1);  // the matrix wave wins issue arbitration over the softmax wave
-          if (do_pv && do_s) fwd_mphase<HD, true, true>(st, sVp, sKc, pb, s);
-          else if (do_s) fwd_mphase<HD, false, true>(st, sVp, sKc, pb, s);
-          else if (do_pv) fwd_mphase<HD, true, false>(st, sVp, sKc, pb, s);
-          __builtin_amdgcn_s_setprio(0);
-        } else {  // softmax of tile jj - 1 (group 1 at h2 = 0) or jj (group 0 at h2 = 1)
-          const int js = jj - 1 + h2;
-          if (js >= 0 && js < ntiles && k_first + js * BN <= st.wmax)
-            fwd_softmax<HD, RING, false>(st, s, k_first + js * BN, sl2, pb);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          if (h2 == 1 && 2 * jj + 1 >= nslots) goto done;
+          if (gp == h2) {  // matrix phase of tile jj
+            const bool do_pv = jj >= 1 && jj <= ntiles && k_first + (jj - 1) * BN <= st.wmax;
+            const bool do_s = jj < ntiles && k_first + jj * BN <= st.wmax;
+            __builtin_amdgcn_s_setprio(1);  // the matrix wave wins issue arbitration over the softmax wave
+            if (do_pv && do_s) fwd_mphase<HD, true, true>(st, sVp, sKc, pb, s);
+            else if (do_s) fwd_mphase<HD, false, true>(st, sVp, sKc, pb, s);
+            else if (do_pv) fwd_mphase<HD, true, false>(st, sVp, sKc, pb, s);
+            __builtin_amdgcn_s_setprio(0);
+          } else {  // softmax of tile jj - 1 (group 1 at h2 = 0) or jj (group 0 at h2 = 1)
+            const int js = jj - 1 + h2;
+            if (js >= 0 && js < ntiles && k_first + js * BN <= st.wmax)
+              fwd_softmax<HD, RING, false>(st, s, k_first + js * BN, sl2, pb);
+          }
+          // Only the end of the tile needs a barrier (the next requests reuse
+          // buffers read in this tile); a second one between the phases, which
+          // only kept the groups in step, cost 1.2%.
+          if (h2 == 1) dma_barrier<0>();
         }
-        // Only the end of the tile needs a barrier (the next requests reuse
-        // buffers read in this tile); a second one between the phases, which
-        // only kept the groups in step, cost 1.2%.
-        if (h2 == 1) dma_barrier<0>();
       }
     }
-  }
-done:
-  if constexpr (FUSED) {
-    // The branch keys, one 64-key tile at a time after the main loop (a few
-    // tiles per unit): S, the softmax masked to each row's own branch keys,
-    // then P V, all in each wave, with no phase offset between the groups.
-    const bf16 *kbg = kb + (int64_t)g * HD;
-    const bf16 *vbtg = vbt + (int64_t)g * (HD * 64);
-    for (int jb = 0; jb < nbt; ++jb) {
-      const int b0 = b_first + jb * BN;
-      dma_barrier<0>();  // every wave is done with buffer 0
-      if (dma_wave) {
-        kt.load(sK0, kbg, b0, (int)mt.Rb - 1);
-        vtt.load(sV0, vbtg + (int64_t)(bt0 + jb) * vt_stride, 0, HD - 1);
-      }
-      dma_barrier<0>();  // the tile is in buffer 0
-      if (b0 <= st.wbmax && b0 + BN - 1 >= st.wbmin) {
-        fwd_mphase<HD, false, true>(st, sV0, sK0, pb, s);
-        fwd_softmax<HD, false, true>(st, s, b0, sl2, pb);
-        fwd_mphase<HD, true, false>(st, sV0, sK0, pb, s);
+  done:
+    if constexpr (FUSED) {
+      // The branch keys, one 64-key tile at a time after the main loop (a few
+      // tiles per unit): S, the softmax masked to each row's own branch keys,
+      // then P V, all in each wave, with no phase offset between the groups.
+      const bf16 *kbg = kb + (int64_t)g * HD;
+      const bf16 *vbtg = vbt + (int64_t)g * (HD * 64);
+      for (int jb = 0; jb < nbt; ++jb) {
+        const int b0 = b_first + jb * BN;
+        dma_barrier<0>();  // every wave is done with buffer 0
+        if (dma_wave) {
+          kt.load(sK0, kbg, b0, (int)mt.Rb - 1);
+          vtt.load(sV0, vbtg + (int64_t)(bt0 + jb) * vt_stride, 0, HD - 1);
+        }
+        dma_barrier<0>();  // the tile is in buffer 0
+        if (b0 <= st.wbmax && b0 + BN - 1 >= st.wbmin) {
+          fwd_mphase<HD, false, true>(st, sV0, sK0, pb, s);
+          fwd_softmax<HD, false, true>(st, s, b0, sl2, pb);
+          fwd_mphase<HD, true, false>(st, sV0, sK0, pb, s);
+        }
       }
     }
-  }
 
-  const float l_tot = half_sum(st.l_run);
-  if constexpr (RING) {
-    // Merge this window's partial into the running (O, LSE) of the row (Eq. 2);
-    // a row that saw no key of the window leaves it unchanged.
-    if (row >= 0 && l_tot > 0.0f) {
-      const int64_t R = mt.Nq + mt.Rb;
-      float *orow = o_run + ((int64_t)row * mt.hq + h) * HD;
-      const float lp = (st.m_run + __log2f(l_tot)) * kLn2;
-      const float la = lse_run[(int64_t)h * R + row];
-      const float M = fmaxf(la, lp);
-      const float wa = __expf(la - M), wb = __expf(lp - M);
-      const float tot = wa + wb;
-      const float fa = wa / tot, fb = wb / (tot * l_tot);
+    const float l_tot = half_sum(st.l_run);
+    if constexpr (RING) {
+      // Merge this window's partial into the running (O, LSE) of the row (Eq. 2);
+      // a row that saw no key of the window leaves it unchanged.
+      if (row >= 0 && l_tot > 0.0f) {
+        const int64_t R = mt.Nq + mt.Rb;
+        float *orow = o_run + ((int64_t)row * mt.hq + h) * HD;
+        const float lp = (st.m_run + __log2f(l_tot)) * kLn2;
+        const float la = lse_run[(int64_t)h * R + row];
+        const float M = fmaxf(la, lp);
+        const float wa = __expf(la - M), wb = __expf(lp - M);
+        const float tot = wa + wb;
+        const float fa = wa / tot, fb = wb / (tot * l_tot);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int d = dt * 32 + q4 * 8 + (lane >> 5) * 4;
+            const f32x4 x = *reinterpret_cast<const f32x4 *>(orow + d);
+            const f32x4 val = {fa * x[0] + fb * st.acc[dt][q4 * 4 + 0], fa * x[1] + fb * st.acc[dt][q4 * 4 + 1],
+                               fa * x[2] + fb * st.acc[dt][q4 * 4 + 2], fa * x[3] + fb * st.acc[dt][q4 * 4 + 3]};
+            *reinterpret_cast<f32x4 *>(orow + d) = val;
+          }
+        if (lane < 32) lse_run[(int64_t)h * R + row] = M + __logf(tot);
+      }
+      return;
+    }
+    if (row >= 0) {
+      const float inv = 1.0f / l_tot;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int d = dt * 32 + q4 * 8 + (lane >> 5) * 4;
-          const f32x4 x = *reinterpret_cast<const f32x4 *>(orow + d);
-          const f32x4 val = {fa * x[0] + fb * st.acc[dt][q4 * 4 + 0], fa * x[1] + fb * st.acc[dt][q4 * 4 + 1],
-                             fa * x[2] + fb * st.acc[dt][q4 * 4 + 2], fa * x[3] + fb * st.acc[dt][q4 * 4 + 3]};
-          *reinterpret_cast<f32x4 *>(orow + d) = val;
+          const f32x4 val = {st.acc[dt][q4 * 4 + 0] * inv, st.acc[dt][q4 * 4 + 1] * inv,
+                             st.acc[dt][q4 * 4 + 2] * inv, st.acc[dt][q4 * 4 + 3] * inv};
+          if (is_main || FUSED) {
+            const bf16x4 b = {(bf16)val[0], (bf16)val[1], (bf16)val[2], (bf16)val[3]};
+            *reinterpret_cast<bf16x4 *>((is_main ? o : ob) + roff + d) = b;
+          } else {
+            *reinterpret_cast<f32x4 *>(o_pre + roff + d) = val;
+          }
         }
-      if (lane < 32) lse_run[(int64_t)h * R + row] = M + __logf(tot);
-    }
-    return;
-  }
-  if (row >= 0) {
-    const float inv = 1.0f / l_tot;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = dt * 32 + q4 * 8 + (lane >> 5) * 4;
-        const f32x4 val = {st.acc[dt][q4 * 4 + 0] * inv, st.acc[dt][q4 * 4 + 1] * inv,
-                           st.acc[dt][q4 * 4 + 2] * inv, st.acc[dt][q4 * 4 + 3] * inv};
-        if (is_main || FUSED) {
-          const bf16x4 b = {(bf16)val[0], (bf16)val[1], (bf16)val[2], (bf16)val[3]};
-          *reinterpret_cast<bf16x4 *>((is_main ? o : ob) + roff + d) = b;
-        } else {
-          *reinterpret_cast<f32x4 *>(o_pre + roff + d) = val;
-        }
+      if (lane < 32) {
+        const float lv = (st.m_run + __log2f(l_tot)) * kLn2;
+        if (is_main) lse[(int64_t)h * mt.Nq + row] = lv;
+        else (FUSED ? lseb : lse_pre)[(int64_t)h * mt.Rb + (row - mt.Nq)] = lv;
       }
-    if (lane < 32) {
-      const float lv = (st.m_run + __log2f(l_tot)) * kLn2;
-      if (is_main) lse[(int64_t)h * mt.Nq + row] = lv;
-      else (FUSED ? lseb : lse_pre)[(int64_t)h * mt.Rb + (row - mt.Nq)] = lv;
     }
+    if (NG != 2 || !mt.queue_units) break;
   }
 }
 
@@ -564,7 +570,7 @@ hipError_t launch_main_fwd_fused_bf16(const Meta &mt, const bf16 *q, const bf16 
   if (mt.n_fwd_pairs == 0) return hipSuccess;
   if (mt.d == 128)
     main_fwd_bf16_kernel<128, false, 2, true>
-        <<<queue_grid((int64_t)mt.n_fwd_pairs * mt.hkv, mt.queue_units), 512, 0, st>>>(
+        <<<persistent_grid((int64_t)mt.n_fwd_pairs * mt.hkv, mt.queue_units), 512, 0, st>>>(
             mt, q, qb, k, vt, o, lse, nullptr, nullptr, 0, 0, nullptr, nullptr, kb, vbt, ob, lseb);
   else
     main_fwd_bf16_kernel<64, false, 3, true>
