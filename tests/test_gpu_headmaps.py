@@ -75,6 +75,10 @@ CASES = {
     "scale0.05_g3_d128": lambda: _case("scg", "bf16", 12, 4, 128, _strided(12, 4), scale=0.05),
     # float32 element type with a strided G = 3 map and a scale
     "f32_g3_strided_scale": lambda: _case("f3", "f32", 6, 2, 128, _strided(6, 2), scale=0.2),
+    # more kv heads than the eight XCDs (the work counters: two home heads per
+    # XCD for some XCDs, one for others)
+    "hkv12_g2_d128": lambda: _case("h12", "bf16", 24, 12, 128),
+    "hkv16_g1_d64_strided": lambda: _case("h16", "bf16", 16, 16, 64, _strided(16, 16)),
 }
 
 
