@@ -184,8 +184,8 @@ __device__ __forceinline__ int lds_off(int row, int d) {  // element offset of (
 template <int BYTES>
 __device__ __forceinline__ void lds_dma(const void *src, const void *lds_dst) {
   static_assert(BYTES == 4 || BYTES == 16, "dword or dwordx4");
-  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane(
-      (int)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_dst);
+  // the LDS offset is the low half of a generic pointer into LDS
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)lds_dst);
   if constexpr (BYTES == 16)
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0)
                  : "memory");
