@@ -231,6 +231,17 @@ __device__ __forceinline__ bf16x8 pad_row_read(const bf16 *tile, uint32_t base, 
   return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(tile) + base +
                                            blk * 32 * kPadRowBytes<HD> + ks * 32);
 }
+// The same two reads from a 32-bit LDS address `a` (tile, lane offset and any
+// row-block offset already added), plus an immediate offset.
+template <int HD>
+__device__ __forceinline__ bf16x8 pad_row_read_at(uint32_t a, int ks) {
+  return *(const __attribute__((address_space(3))) bf16x8 *)(uintptr_t)(a + ks * 32);
+}
+template <int HD>
+__device__ __forceinline__ i16x4 pad_tr_read_at(uint32_t a, int c, int kk, int dt) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4 *)(uintptr_t)(a + (16 * kk + 8 * c) * kPadRowBytes<HD> + dt * 64));
+}
 // Transposing read (operand with k = row): the 16-lane group g = lane/16 reads
 // rows 16*kk + 4*(g/2) + (lane%16)/4 + 8c, columns 32*dt + 16*(g%2) + 4*(lane%4) .. +3.
 template <int HD>

@@ -417,9 +417,23 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
                                           const float *sD, const int *sEnd) {
   constexpr int BM = kTileRows;
   constexpr int KS = DkdvState<HD, KB>::KS, DT = DkdvState<HD, KB>::DT;
+  // dO follows Q in the same array; the second buffer starts beyond the reach
+  // of an LDS read's 16-bit offset, so with the addresses left to constant
+  // folding every read of it took an add of its own. Instead each row block
+  // forms its two Q addresses (row and transposing reads: tile, lane offset,
+  // row block) once, kept opaque, and every read is one of them plus an
+  // immediate (dO at a fixed distance).
+  constexpr uint32_t kOff = BM * kPadRowBytes<HD>;  // dO - Q, bytes
+  uint32_t a_r = st.r_base, a_t = st.t_base;
+  asm volatile("" : "+v"(a_r), "+v"(a_t));  // formed here, not hoisted out of the tile loop and spilled
+  a_r += (uint32_t)(uintptr_t)sQ;
+  a_t += (uint32_t)(uintptr_t)sQ;
+  (void)sdO;
 #pragma unroll 1
   for (int rb = 0; rb < BM / 32; ++rb) {
     const int lane = lane_id_here();
+    uint32_t q_r = a_r + rb * 32 * kPadRowBytes<HD>, q_t = a_t + rb * 32 * kPadRowBytes<HD>;
+    asm volatile("" : "+v"(q_r), "+v"(q_t));
     // Rows 32rb..32rb+31. element i: row rb*32 + (i/4)*8 + 4*(lane/32) + i%4,
     // key my_key[b].
     bf16x8 pa[KB][2], dsa[KB][2];
@@ -428,9 +442,9 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
     // Operand slot 8*half + 4c + j <-> row 32rb + 16kh + 8c + 4*half + j.
     constexpr int NS = 2 * DT;
     auto rd = [&](int i) {
-      const int n = i % NS, kk = 2 * rb + n / DT, dt = n % DT;
-      const bf16 *t = i < NS ? sdO : sQ;
-      return join(pad_tr_read<HD>(t, st.t_base, 0, kk, dt), pad_tr_read<HD>(t, st.t_base, 1, kk, dt));
+      const int n = i % NS, kk = n / DT, dt = n % DT;
+      const uint32_t t = i < NS ? q_t + kOff : q_t;
+      return join(pad_tr_read_at<HD>(t, 0, kk, dt), pad_tr_read_at<HD>(t, 1, kk, dt));
     };
     bf16x8 ring[kDkdvRing];
     {
@@ -441,11 +455,15 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
       // by scale * log2(e), so the S MFMAs deliver the exponent of P.
       f32x16 sc[KB], dp[KB];
       f32x16 nd, nl;
+      // the row block's -D and -LSE entries, from two opaque addresses plus
+      // immediates (these arrays too lie beyond the reads' offset reach)
+      uint32_t a_d = (uint32_t)(uintptr_t)sD + rb * 128 + 16 * (lane >> 5);
+      uint32_t a_l = (uint32_t)(uintptr_t)sL2 + rb * 128 + 16 * (lane >> 5);
+      asm volatile("" : "+v"(a_d), "+v"(a_l));
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const int r0 = rb * 32 + i4 * 8 + 4 * (lane >> 5);
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(sD + r0);
-        const f32x4 y = *reinterpret_cast<const f32x4 *>(sL2 + r0);
+        const f32x4 x = *(const __attribute__((address_space(3))) f32x4 *)(uintptr_t)(a_d + i4 * 32);
+        const f32x4 y = *(const __attribute__((address_space(3))) f32x4 *)(uintptr_t)(a_l + i4 * 32);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           nd[i4 * 4 + e] = x[e];
@@ -460,14 +478,14 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
       __builtin_amdgcn_s_setprio(1);  // a wave in an MFMA stretch wins issue; the other wave's VALU fills in
       // The operands of step ks + 1 are read while step ks multiplies.
       bf16x8 aq[2], ao[2];
-      aq[0] = pad_row_read<HD>(sQ, st.r_base, rb, 0);
-      ao[0] = pad_row_read<HD>(sdO, st.r_base, rb, 0);
+      aq[0] = pad_row_read_at<HD>(q_r, 0);
+      ao[0] = pad_row_read_at<HD>(q_r + kOff, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if (ks + 1 < KS) {
-          aq[(ks + 1) & 1] = pad_row_read<HD>(sQ, st.r_base, rb, ks + 1);
-          ao[(ks + 1) & 1] = pad_row_read<HD>(sdO, st.r_base, rb, ks + 1);
+          aq[(ks + 1) & 1] = pad_row_read_at<HD>(q_r, ks + 1);
+          ao[(ks + 1) & 1] = pad_row_read_at<HD>(q_r + kOff, ks + 1);
         }
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
