@@ -258,20 +258,16 @@ __device__ __forceinline__ i16x4 pad_tr_read(const bf16 *tile, uint32_t base, in
 // Per-lane addressing of MFMA operand reads from a swizzled [row][HD] bf16 LDS
 // tile. The swizzle XORs chunk-index bits that the k-step (or d-block) index
 // and the lane's own chunk bits never share, so an operand's byte offset is
-// (step << c) ^ t plus a per-lane row base: one xad per read from two
-// registers, instead of one precomputed address register per step.
+// (step << c) ^ t plus a per-lane row base.
 //
 // Row read (ds_read_b128, A operand with k = d): lane reads row
-// 32*blk + r (r = lane % 32 plus a caller offset), chunk 2*ks + lane/32.
+// 32*blk + r (r = lane % 32 plus a caller offset), chunk 2*ks + lane/32, at
+// byte base + ((ks << 5) ^ t) + blk * 32 * HD * 2 (the forward keeps the first
+// two terms per ks in registers, so a read is a register plus an immediate).
 template <int HD>
 __device__ __forceinline__ void row_read_init(int r, int lane, uint32_t &base, uint32_t &t) {
   base = (uint32_t)(r * HD * 2);
   t = (uint32_t)((lane >> 5) ^ swz<HD>(r)) << 4;
-}
-template <int HD>
-__device__ __forceinline__ bf16x8 row_read(const bf16 *tile, uint32_t base, uint32_t t, int blk, int ks) {
-  const uint32_t off = base + (((uint32_t)ks << 5) ^ t) + (uint32_t)(blk * 32 * HD * 2);
-  return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(tile) + off);
 }
 // Transposing read (ds_read_b64_tr_b16, operand with k = row): the 16-lane
 // group g = lane/16 reads rows 16*kk + 4*(g/2) + (lane%16)/4 + 8c, d = 32*dt +

@@ -61,6 +61,9 @@ struct FwdState {
   int lane;
   uint32_t k_base, k_t;  // K row reads
   uint32_t v_base, v_t;  // V^T row reads
+  // the swizzled byte offset of each k-step's K and V^T read, formed once, so a
+  // read is a register plus an immediate (no XOR and add per read)
+  uint32_t k_off[KS], v_off[4];
 };
 
 // Matrix phase: O^T += V^T P^T for the previous K/V tile (PV), then the raw
@@ -86,9 +89,12 @@ __device__ __forceinline__ void fwd_mphase(FwdState<HD> &st, const bf16 *sVt, co
   constexpr int N = NPV + NS;
   constexpr int R = fwd_ring(HD) < N ? fwd_ring(HD) : N;
   auto rd = [&](int i) -> bf16x8 {
-    if (i < NPV) return row_read<64>(sVt, st.v_base, st.v_t, i % DT, i / DT);
+    if (i < NPV)
+      return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(sVt) + st.v_off[i / DT] +
+                                               (i % DT) * 32 * 64 * 2);
     const int j = i - NPV;
-    return row_read<HD>(sK, st.k_base, st.k_t, j % 2, j / 2);
+    return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(sK) + st.k_off[j / 2] +
+                                             (j % 2) * 32 * HD * 2);
   };
   if constexpr (S) {
     s[0] = f32x16{};
@@ -332,6 +338,10 @@ __global__ __launch_bounds__(256 * NG, 1) void main_fwd_bf16_kernel(Meta mt, con
     st.lane = lane;
     row_read_init<HD>(lane & 31, lane, st.k_base, st.k_t);
     row_read_init<64>(lane & 31, lane, st.v_base, st.v_t);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) st.k_off[ks] = st.k_base + (((uint32_t)ks << 5) ^ st.k_t);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) st.v_off[kk] = st.v_base + (((uint32_t)kk << 5) ^ st.v_t);
     const float sl2 = mt.scale * kLog2e;
 
     // K tiles: 64 keys x d from the [N][Hkv][d] tensor; V^T tiles: d rows x 64
