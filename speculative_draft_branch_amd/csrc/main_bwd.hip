@@ -594,6 +594,7 @@ __global__ __launch_bounds__(dkdv_threads(HD), 1) void main_bwd_dkdv_bf16_kernel
   // before it, which would otherwise include this tile's Q and dO rows.
   auto prefetch = [&](int qi, bf16 *sQ, bf16 *sO, float *sL, float *sD, int *sE) {
     const int64_t tb = ((int64_t)qi * hkv + g) * BM;
+    const int lane = lane_id_here();  // per-lane source addresses formed here, not kept across the tile loop
     if (wave == 0) stage_words_async<BM / 64>(sL, lt + tb, lane);
     else if (wave == 1) stage_words_async<BM / 64>(sD, dtt + tb, lane);
     else if (wave == 2) stage_words_async<kTileMetaWords / 64>(sE, et + (int64_t)qi * kTileMetaWords, lane);
