@@ -395,7 +395,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only: the path runs one GPU's share; "
+        print(json.dumps({"error": "bench.py measures one GPU only: the path runs one GPU's share; "
                                    "run with --gpus 1", "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
