@@ -588,10 +588,9 @@ __global__ __launch_bounds__(dkdv_threads(HD), 1) void main_bwd_dkdv_bf16_kernel
   const int g = item % hkv;
   const KTile kt = load_ktile(mt.ktiles + uni(mt.bwd_order[item / hkv]));
 
-  // Query tile qi, kv head g -> one LDS buffer (all asynchronous). The row
-  // metadata goes first: an address the compiler keeps in scratch is reloaded
-  // there, and waiting for that reload waits (in order) for every load issued
-  // before it, which would otherwise include this tile's Q and dO rows.
+  // Query tile qi, kv head g -> one LDS buffer (all asynchronous; the next tile
+  // barrier waits for it): the row metadata (-LSE, -D, row ends) by waves 0-2,
+  // the Q and dO rows by the NSW staging waves.
   auto prefetch = [&](int qi, bf16 *sQ, bf16 *sO, float *sL, float *sD, int *sE) {
     const int64_t tb = ((int64_t)qi * hkv + g) * BM;
     const int lane = lane_id_here();  // per-lane source addresses formed here, not kept across the tile loop
