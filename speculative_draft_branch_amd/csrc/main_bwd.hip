@@ -371,8 +371,11 @@ __global__ __launch_bounds__(256 * NG, 1) void main_bwd_dq_bf16_kernel(Meta mt, 
     dma_barrier<0>();  // the tile is in buffer 0
     if (b0 <= wbmax && b0 + BN - 1 >= wbmin) dq_tile<HD, true, true>(st, sK0, sV0, b0, sl2, sBrw + (lane & 31));
   }
-  if (row >= 0) {
-    bf16 *dst = (is_main ? dq : dqb) + roff;
+  // The row's offset again from the LDS table, so that none of the row's
+  // addressing is kept in registers across the key loops.
+  const int64_t ridx = sRowIdx[uni(threadIdx.x >> 6) * 32 + (lane_id_here() & 31)];
+  if (ridx != -1) {
+    bf16 *dst = (ridx >= 0 ? dq + ridx * HD : dqb + (-2 - ridx) * HD);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
