@@ -122,7 +122,7 @@ __device__ __forceinline__ void dq_tile(DqState<HD> &st, const bf16 *sK, const b
 #pragma unroll
     for (int i = 0; i < kDqKRing; ++i) kr[i] = rdk(i);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(2);  // above an S/dP stretch: a wave that has its products ready goes first
 #pragma unroll
     for (int n = 0; n < 2 * DT; ++n) {
       st.acc[n % DT] = mfma32(kr[n % kDqKRing], db[n / DT], st.acc[n % DT]);
@@ -523,7 +523,7 @@ __device__ __forceinline__ void dkdv_rows(DkdvState<HD, KB> &st, const bf16 *sQ,
     // dV += P^T dO, dK += dS^T Q over these 32 rows (two 16-row k-steps): all
     // dV steps, then all dK steps, through one ring of kDkdvRing operands, a
     // read issued kDkdvRing - 1 MFMAs before its use.
-    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(2);  // above an S/dP stretch of the other wave
     {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
