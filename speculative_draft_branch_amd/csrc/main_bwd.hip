@@ -638,17 +638,17 @@ __global__ __launch_bounds__(dkdv_threads(HD), 1) void main_bwd_dkdv_bf16_kernel
 
   // Waves 0-3 (the older wave of each SIMD, which wins issue ties and would
   // otherwise run ahead, then wait at the next barrier) start each tile about
-  // 256 cycles after the others.
+  // 128 cycles after the others.
   const bool delay = uni(wave) < 4;
   for (int qi = kt.qt_begin; qi < kt.qt_end; qi += 2) {
     dma_barrier<0>();  // tile qi is in buffer 0; every wave is done with buffer 1
     if (qi + 1 < kt.qt_end) prefetch(qi + 1, sQ1, sO1, sL1, sD1, sE1);
-    if (delay) __builtin_amdgcn_s_sleep(4);
+    if (delay) __builtin_amdgcn_s_sleep(2);
     dkdv_tile<HD, KB>(st, sQ0, sO0, sL0, sD0, sE0);
     if (qi + 1 >= kt.qt_end) break;
     dma_barrier<0>();  // tile qi+1 is in buffer 1; every wave is done with buffer 0
     if (qi + 2 < kt.qt_end) prefetch(qi + 2, sQ0, sO0, sL0, sD0, sE0);
-    if (delay) __builtin_amdgcn_s_sleep(4);
+    if (delay) __builtin_amdgcn_s_sleep(2);
     dkdv_tile<HD, KB>(st, sQ1, sO1, sL1, sD1, sE1);
   }
 
