@@ -105,9 +105,13 @@ __device__ __forceinline__ void fwd_mphase(FwdState<HD> &st, const bf16 *sVt, co
   bf16x8 ring[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) ring[i] = rd(i);
+  // The S steps, whose scores the wave's own next softmax phase waits for,
+  // run at priority 2, the P V steps at the caller's 1.
+  if (!PV) __builtin_amdgcn_s_setprio(2);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < N; ++i) {
+    if (PV && S && i == NPV) __builtin_amdgcn_s_setprio(2);
     if (i < NPV) {
       st.acc[i % DT] = mfma32(ring[i % R], pb[i / DT], st.acc[i % DT]);
     } else {
