@@ -422,6 +422,7 @@ __global__ __launch_bounds__(256 * NG, 1) void main_fwd_bf16_kernel(Meta mt, con
         dma_barrier<0>();  // the tile is in buffer 0
         if (b0 <= st.wbmax && b0 + BN - 1 >= st.wbmin) {
           fwd_mphase<HD, false, true>(st, sV0, sK0, pb, s);
+          __builtin_amdgcn_s_setprio(0);  // the S steps raised it; no phase offset here
           fwd_softmax<HD, false, true>(st, s, b0, sl2, pb);
           fwd_mphase<HD, true, false>(st, sV0, sK0, pb, s);
         }
