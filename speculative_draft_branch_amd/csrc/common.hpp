@@ -159,13 +159,18 @@ __device__ __forceinline__ int wave_max(int x) {
   return x;
 }
 
-// LDS tiles of key rows (d bf16 each) are stored in 16-byte chunks whose index
-// is XOR-swizzled by the row, so that both the row-wise 16-byte reads of the
-// K operand and the 4-row transposed reads of the V operand spread over banks.
+// LDS tiles of key rows (HD bf16 each: 256-byte rows at HD = 128, 128-byte rows
+// for HD = 64 and for the 64-key V^T tiles) are stored in 16-byte chunks whose
+// index is XOR-swizzled by the row, so that the row-wise 16-byte operand reads
+// (16 rows at one chunk) and the transposing reads (4 rows x 4 chunks) spread
+// over the 64 banks. A 128-byte row shares its bank line with the next row, so
+// its swizzle is a bijection of row bits 1-3 (even and odd rows each get eight
+// distinct chunks), with bit 2 following row bit 1 for the transposing reads;
+// the bank counters read zero conflicts for both patterns with it.
 template <int HD>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (HD == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
-  else return ((row & 3) << 1) | ((row >> 2) & 1);
+  else return (((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
 }
 template <int HD>
 __device__ __forceinline__ int lds_off(int row, int d) {  // element offset of (row, d)
